@@ -1,0 +1,59 @@
+"""Algorithmic FLOP and byte model used by the benchmark's roofline figures.
+
+* Compute stays Theta(N^2 d) under the method (page "ZeRO 与 FlashAttention 各优化什么?",
+  section "FlashAttention 与 ZeRO 必须分开": the dense FLOPs do not become linear).
+  Forward = two N x N x d contractions (S = Q K^T and O = P V) = 4 B Hq N^2 d flop,
+  halved for causal attention.
+* Backward = 2.5 x forward: five N x N x d contractions (recomputed S, dP, dV, dK,
+  dQ) against the forward's two, in the 2.2-2.5x range that the interview bank
+  ch.029 question #36 gives for FlashAttention's backward.
+* Compulsory HBM traffic: every input read once and every output written once;
+  nothing of size N x N (the score matrix never reaches HBM).
+* The score-matrix sizes the pages quote (code-corey Q38 section 1: 8K x 8K x 4 B
+  ~ 256 MB; interview bank #36 section 2: 32 x 4096 x 4096 x 4 B ~ 2.1 GB) and the
+  KV saving of grouped-query attention (lecture summary section "减少缓存表示并验证草稿":
+  24 query heads over 2 KV groups, about 91 %) are reproduced by the helpers below.
+"""
+from __future__ import annotations
+
+# MI355X published peaks (AMD specifications): dense bf16 MFMA, fp32 vector and HBM3E.
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_FP32_VECTOR_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def fwd_flops(B, Hq, N, d, causal: bool) -> float:
+    f = 4.0 * B * Hq * N * N * d
+    return f / 2 if causal else f
+
+
+def bwd_flops(B, Hq, N, d, causal: bool) -> float:
+    return 2.5 * fwd_flops(B, Hq, N, d, causal)
+
+
+def fwd_bytes(B, Hq, Hkv, N, d, elt: int) -> int:
+    """Read Q, K, V once; write O and the fp32 LSE once."""
+    return elt * (2 * B * Hq * N * d + 2 * B * Hkv * N * d) + 4 * B * Hq * N
+
+
+def bwd_bytes(B, Hq, Hkv, N, d, elt: int) -> int:
+    """Read Q, O, dO, K, V, LSE; write dQ, dK, dV; D (fp32 per row) written and read."""
+    q_sized = B * Hq * N * d
+    kv_sized = B * Hkv * N * d
+    return elt * (3 * q_sized + 2 * kv_sized) + 4 * B * Hq * N \
+        + elt * (q_sized + 2 * kv_sized) + 2 * 4 * B * Hq * N
+
+
+def preprocess_bytes(B, Hq, N, d, elt: int) -> int:
+    """The backward preprocess reads O and dO and writes one fp32 D per row."""
+    return 2 * elt * B * Hq * N * d + 4 * B * Hq * N
+
+
+def score_matrix_bytes(N, elt: int = 4, heads: int = 1, batch: int = 1) -> int:
+    """Size of one materialised N x N score matrix per head (what the method avoids)."""
+    return batch * heads * N * N * elt
+
+
+def kv_storage_saving(Hq, Hkv) -> float:
+    """Fraction of K/V storage saved by Hkv shared heads versus Hq (MHA)."""
+    return 1.0 - Hkv / Hq

@@ -1,0 +1,225 @@
+"""CPU float64 oracle for exact scaled dot-product attention, forward and backward.
+
+TEST INFRASTRUCTURE ONLY. The tests, the package's ``smoke()`` check and the
+CPU-baseline leg of the benchmark may import this module; the HIP library and its
+Python binding never do. It shares no code, tables or helpers with the GPU path.
+
+What it computes is the plain definition of attention, written out:
+
+    S = scale * Q K^T            (one query head against the KV head of its group)
+    S_ij = -inf  where j > i     (causal: a token sees itself and earlier tokens)
+    P = softmax(S) row-wise,  O = P V,  LSE_i = log sum_j exp(S_ij)
+
+Sources, cited by page title and section:
+
+* "ZeRO 与 FlashAttention 各优化什么?" (wushixiongai.com), section
+  "注意力瓶颈与优化路线": FlashAttention / fused SDPA computes *exact* dense attention;
+  tiling, online softmax and fusion change only where and in which order it is computed.
+* Stanford lecture summary (youtublog.net), section "GPU 显存和注意力瓶颈": in causal
+  self-attention each token attends to itself and the tokens before it (mask j <= i,
+  diagonal included).  Section "推导 FlashAttention 的在线 softmax": an output row is a
+  numerator (sum of exp(score) * value) over a denominator (sum of exp(score)); the
+  method keeps a small per-row statistic for the backward pass.  Section
+  "减少缓存表示并验证草稿": H query heads share G key/value heads (G = H is MHA, G = 1
+  is MQA).
+* "LLM interview question bank" ch.029 (ricardokevins.github.io), question #36
+  "FlashAttention 为什么常被说成是 IO-aware", section 2: Q, K, V live in R^(B x H x L x d).
+
+Readings where the pages are silent (each listed with its reason in the design notes):
+
+* The scale is the caller's (configs pass 1/sqrt(d)).
+* The saved statistic is the natural-log log-sum-exp of the *scaled* logits.
+* Query head hq uses KV head hq // (Hq / Hkv) (contiguous groups).
+* The gradients are the analytic softmax-Jacobian gradients (the pages print none):
+      dP = dO V^T,  D_i = sum_j P_ij dP_ij,  dS = P * (dP - D),
+      dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO,
+  with dK and dV of a KV head summed over the query heads of its group.
+
+Rows are processed in blocks, but each block holds *full* rows of S and P
+(the two-pass softmax of the definition, not an online one), so nothing here is
+blocked, fused or reordered beyond what a BLAS matmul does internally.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ProcessPoolExecutor
+
+import numpy as np
+
+ROW_BLOCK = 512
+
+
+def _f64(x) -> np.ndarray:
+    """Upcast anything array-like (numpy or a CPU torch tensor) to float64 numpy."""
+    if hasattr(x, "detach"):  # torch tensor; bf16 has no numpy dtype, go via float32
+        x = x.detach().to("cpu")
+        if str(x.dtype) in ("torch.bfloat16", "torch.float16"):
+            x = x.float()
+        x = x.numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _scores(q_rows: np.ndarray, k: np.ndarray, rows: np.ndarray, causal: bool, scale: float):
+    """S for the given query rows against all keys, with the causal mask applied."""
+    s = scale * (q_rows @ k.T)
+    if causal:
+        cols = np.arange(k.shape[0])
+        s = np.where(cols[None, :] <= rows[:, None], s, -np.inf)
+    return s
+
+
+def head_forward(q, k, v, causal: bool, scale: float, rows=None):
+    """One query head: O and LSE for the selected query rows (default: all rows).
+
+    q: [N, d]; k, v: [N, d] (the KV head of this query's group).  Returns
+    (O [len(rows), d], LSE [len(rows)]) in float64.  A row with no visible key
+    (not reachable when queries and keys have the same length) gives O = 0 and
+    LSE = -inf.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n = q.shape[0]
+    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.zeros((rows.size, v.shape[1]))
+    lse = np.full(rows.size, -np.inf)
+    for b0 in range(0, rows.size, ROW_BLOCK):
+        r = rows[b0:b0 + ROW_BLOCK]
+        s = _scores(q[r], k, r, causal, scale)
+        m = s.max(axis=1)                              # pass 1: row max
+        ok = np.isfinite(m)
+        e = np.exp(s - np.where(ok, m, 0.0)[:, None])  # pass 2: exponentials
+        l = e.sum(axis=1)
+        p = e / np.where(ok, l, 1.0)[:, None]
+        o[b0:b0 + r.size] = np.where(ok[:, None], p @ v, 0.0)
+        lse[b0:b0 + r.size] = np.where(ok, m + np.log(np.where(ok, l, 1.0)), -np.inf)
+    return o, lse
+
+
+def head_probs(q, k, causal: bool, scale: float):
+    """The full softmax matrix P [N, N] of one head (small inputs only)."""
+    q, k = _f64(q), _f64(k)
+    rows = np.arange(q.shape[0])
+    s = _scores(q, k, rows, causal, scale)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def head_backward(q, k, v, do, causal: bool, scale: float):
+    """One query head: (dQ, dK, dV) for L = sum(dO * O), float64.
+
+    dK and dV are this head's contribution to its KV head; the caller sums them
+    over the query heads of a group.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    n = q.shape[0]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b0 in range(0, n, ROW_BLOCK):
+        r = np.arange(b0, min(n, b0 + ROW_BLOCK))
+        s = _scores(q[r], k, r, causal, scale)
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        p = e / e.sum(axis=1, keepdims=True)          # P, full rows
+        dp = do[r] @ v.T                              # dP = dO V^T
+        dvec = (p * dp).sum(axis=1, keepdims=True)    # D_i = sum_j P_ij dP_ij
+        ds = p * (dp - dvec)                          # dS = P * (dP - D)
+        dq[r] = scale * (ds @ k)
+        dk += scale * (ds.T @ q[r])
+        dv += p.T @ do[r]
+    return dq, dk, dv
+
+
+# --------------------------------------------------------------------------- batched
+
+def _group(hq: int, hq_total: int, hkv_total: int) -> int:
+    """KV head used by query head hq: contiguous groups of Hq/Hkv query heads."""
+    return hq // (hq_total // hkv_total)
+
+
+def _check_shapes(q, k, v):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("expected [B, H, N, d] arrays")
+    b, hq, n, d = q.shape
+    if k.shape != v.shape or k.shape[0] != b or k.shape[2] != n or k.shape[3] != d:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    if hq % k.shape[1] != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+
+
+def _fwd_unit(args):
+    q, k, v, causal, scale, rows = args
+    return head_forward(q, k, v, causal, scale, rows)
+
+
+def _bwd_unit(args):
+    q, k, v, do, causal, scale = args
+    return head_backward(q, k, v, do, causal, scale)
+
+
+def _pool(workers: int):
+    # One BLAS thread per worker process; the environment is inherited by the
+    # workers, which load their BLAS after this point.
+    os.environ.setdefault("OPENBLAS_NUM_THREADS", "1")
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    return ProcessPoolExecutor(max_workers=workers)
+
+
+def attention_forward(q, k, v, causal: bool, scale: float, heads=None, rows=None, workers: int = 1):
+    """O [B,Hq,N,d] and LSE [B,Hq,N] (float64) for every (b, hq) in ``heads``.
+
+    ``heads`` is an iterable of (b, hq) pairs (default: all); entries of heads not
+    listed are NaN.  ``rows`` optionally restricts the computed query rows (the same
+    rows for every listed head).  ``workers`` > 1 runs heads in a process pool.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    _check_shapes(q, k, v)
+    b_, hq_, n, d = q.shape
+    hkv_ = k.shape[1]
+    heads = [(b, h) for b in range(b_) for h in range(hq_)] if heads is None else list(heads)
+    o = np.full(q.shape, np.nan)
+    lse = np.full(q.shape[:3], np.nan)
+    jobs = [(q[b, h], k[b, _group(h, hq_, hkv_)], v[b, _group(h, hq_, hkv_)], causal, scale, rows)
+            for b, h in heads]
+    if workers > 1 and len(jobs) > 1:
+        with _pool(workers) as ex:
+            results = list(ex.map(_fwd_unit, jobs))
+    else:
+        results = [_fwd_unit(j) for j in jobs]
+    sel = slice(None) if rows is None else np.asarray(rows)
+    for (b, h), (ob, lb) in zip(heads, results):
+        o[b, h, sel] = ob
+        lse[b, h, sel] = lb
+    return o, lse
+
+
+def attention_backward(q, k, v, do, causal: bool, scale: float, groups=None, workers: int = 1):
+    """dQ [B,Hq,N,d], dK and dV [B,Hkv,N,d] (float64) for the listed (b, hkv) groups.
+
+    A group's dK/dV is the sum over its Hq/Hkv query heads; the dQ of every query
+    head in a listed group is filled.  Entries outside the listed groups are NaN.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    _check_shapes(q, k, v)
+    b_, hq_, n, d = q.shape
+    hkv_ = k.shape[1]
+    g = hq_ // hkv_
+    groups = [(b, h) for b in range(b_) for h in range(hkv_)] if groups is None else list(groups)
+    dq = np.full(q.shape, np.nan)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(v.shape, np.nan)
+    units = [(b, hk, h) for b, hk in groups for h in range(hk * g, hk * g + g)]
+    jobs = [(q[b, h], k[b, hk], v[b, hk], do[b, h], causal, scale) for b, hk, h in units]
+    if workers > 1 and len(jobs) > 1:
+        with _pool(workers) as ex:
+            results = list(ex.map(_bwd_unit, jobs))
+    else:
+        results = [_bwd_unit(j) for j in jobs]
+    for b, hk in groups:
+        dk[b, hk] = 0.0
+        dv[b, hk] = 0.0
+    for (b, hk, h), (dqh, dkh, dvh) in zip(units, results):
+        dq[b, h] = dqh
+        dk[b, hk] += dkh
+        dv[b, hk] += dvh
+    return dq, dk, dv
