@@ -1,0 +1,142 @@
+"""Python binding of libfa_mi355x.so (ctypes): argument marshalling only.
+
+torch provides device memory and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from pathlib import Path
+
+import torch
+
+LIB_PATH = Path(os.environ.get("FA_MI355X_LIB", Path(__file__).resolve().parent / "libfa_mi355x.so"))
+
+FA_STATUS = {
+    0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_GQA", 4: "FA_ERR_HEADDIM",
+    5: "FA_ERR_SCALE", 6: "FA_ERR_ALIGN", 7: "FA_ERR_FLAG", 8: "FA_ERR_WORKSPACE",
+    9: "FA_ERR_ALIAS", 10: "FA_ERR_LAUNCH",
+}
+ENTRY_POINTS = ("fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_workspace_bytes",
+                "fa_check_args", "fa_status_string")
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} returned {FA_STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        raise FileNotFoundError(f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_20_amd.build`")
+    lib = ctypes.CDLL(str(LIB_PATH))
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_forward.restype = i
+    lib.fa_forward_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_forward_f32.restype = i
+    lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
+    lib.fa_backward.restype = i
+    lib.fa_backward_workspace_bytes.argtypes = [i, i, i]
+    lib.fa_backward_workspace_bytes.restype = sz
+    lib.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i]
+    lib.fa_check_args.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load_library().fa_status_string(code).decode()
+
+
+def _check(fn: str, code: int):
+    if code != 0:
+        raise FAError(fn, code, status_string(code))
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _shape(q: torch.Tensor, k: torch.Tensor):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, Hq, N, d = q.shape
+    return B, Hq, k.shape[1], N, d
+
+
+def _require(t: torch.Tensor, name: str, dtype, shape):
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device} contiguous={t.is_contiguous()}")
+
+
+def forward(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None):
+    """bf16 forward via fa_forward.  Returns (o, lse); o bf16 [B,Hq,N,d], lse fp32 [B,Hq,N]."""
+    return _forward("fa_forward", torch.bfloat16, q, k, v, causal, scale, o, lse, stream)
+
+
+def forward_f32(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None):
+    """fp32 forward via fa_forward_f32."""
+    return _forward("fa_forward_f32", torch.float32, q, k, v, causal, scale, o, lse, stream)
+
+
+def _forward(fn, dtype, q, k, v, causal, scale, o, lse, stream):
+    lib = load_library()
+    B, Hq, Hkv, N, d = _shape(q, k)
+    _require(q, "q", dtype, (B, Hq, N, d))
+    _require(k, "k", dtype, (B, Hkv, N, d))
+    _require(v, "v", dtype, (B, Hkv, N, d))
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _require(o, "o", dtype, (B, Hq, N, d))
+    _require(lse, "lse", torch.float32, (B, Hq, N))
+    code = getattr(lib, fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            B, Hq, Hkv, N, d, int(causal), float(scale), _stream(stream))
+    _check(fn, code)
+    return o, lse
+
+
+def workspace_bytes(B: int, Hq: int, N: int) -> int:
+    return int(load_library().fa_backward_workspace_bytes(B, Hq, N))
+
+
+def backward(q, k, v, o, do, lse, causal: bool, scale: float, dq=None, dk=None, dv=None,
+             workspace=None, stream=None):
+    """bf16 backward via fa_backward.  Returns (dq, dk, dv)."""
+    lib = load_library()
+    B, Hq, Hkv, N, d = _shape(q, k)
+    for t, name, shp in ((q, "q", (B, Hq, N, d)), (k, "k", (B, Hkv, N, d)), (v, "v", (B, Hkv, N, d)),
+                         (o, "o", (B, Hq, N, d)), (do, "do", (B, Hq, N, d))):
+        _require(t, name, torch.bfloat16, shp)
+    _require(lse, "lse", torch.float32, (B, Hq, N))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _require(dq, "dq", torch.bfloat16, (B, Hq, N, d))
+    _require(dk, "dk", torch.bfloat16, (B, Hkv, N, d))
+    _require(dv, "dv", torch.bfloat16, (B, Hkv, N, d))
+    nbytes = workspace_bytes(B, Hq, N)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    code = lib.fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           B, Hq, Hkv, N, d, int(causal), float(scale), _stream(stream))
+    _check("fa_backward", code)
+    return dq, dk, dv

@@ -1,0 +1,121 @@
+/*
+ * fa.h: C ABI of libfa_mi355x.so, exact IO-aware attention for MI355X (gfx950).
+ *
+ * What is computed (the plain definition; the kernels reach it up to rounding):
+ *
+ *   for every batch b, query head hq and query row i, with g = hq / (Hq / Hkv):
+ *     s_ij   = scale * sum_t Q[b,hq,i,t] * K[b,g,j,t]       over visible keys j
+ *     visible: all j < N, or j <= i when causal
+ *     O[b,hq,i,:] = sum_j softmax_j(s_ij) * V[b,g,j,:]
+ *     LSE[b,hq,i] = log(sum_j exp(s_ij))                     (natural log, fp32)
+ *
+ * Sources (page title, section):
+ *   - "ZeRO 与 FlashAttention 各优化什么?" (wushixiongai.com), "注意力瓶颈与优化路线":
+ *     FlashAttention / fused SDPA computes exact dense attention with tiling, online
+ *     softmax and fusion, cutting HBM traffic and auxiliary storage.
+ *   - "LLM interview question bank" ch.029 (ricardokevins.github.io), #36
+ *     "FlashAttention 为什么常被说成是 IO-aware", sections 2-3: Q, K, V in
+ *     R^(B x H x L x d); Q tiles loop over K/V tiles held on chip with running
+ *     (m, l) statistics; the score tile is never written to HBM.
+ *   - Stanford lecture summary (youtublog.net): "GPU 显存和注意力瓶颈" (causal: a token
+ *     attends to itself and earlier tokens), "推导 FlashAttention 的在线 softmax"
+ *     (rescaled numerator/denominator; the backward pass recomputes from a small
+ *     saved statistic), "减少缓存表示并验证草稿" (H query heads share G KV heads).
+ *
+ * Conventions for every entry point:
+ *   - Device pointers, contiguous row-major tensors with the head dimension d
+ *     fastest: Q, O, dO, dQ are [B, Hq, N, d]; K, V, dK, dV are [B, Hkv, N, d];
+ *     LSE is [B, Hq, N] fp32.  Every pointer must be 16-byte aligned.
+ *   - Hq must be a multiple of Hkv; query head hq reads KV head hq / (Hq/Hkv)
+ *     (contiguous groups).  d must be 64 or 128.  B, Hq, Hkv, N >= 1.
+ *   - scale must be finite and >= 0.  causal must be 0 or 1.
+ *   - The caller allocates and frees all memory.  The library allocates nothing,
+ *     keeps no mutable global state and never synchronises: work is enqueued on
+ *     `stream` (0 = the null stream) and results are valid after the caller
+ *     synchronises that stream.  Outputs must not overlap inputs or each other.
+ *   - Arguments are validated on the host before anything is launched; on error
+ *     nothing is launched and no output is touched.  FA_ERR_LAUNCH reports a
+ *     launch failure seen by hipGetLastError; faults inside a kernel surface at
+ *     the caller's next synchronisation, as usual for HIP.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,       /* a required pointer is NULL                        */
+    FA_ERR_SHAPE = 2,      /* B, Hq, Hkv or N < 1, or the launch grid too large  */
+    FA_ERR_GQA = 3,        /* Hq is not a multiple of Hkv                        */
+    FA_ERR_HEADDIM = 4,    /* d is not 64 or 128                                 */
+    FA_ERR_SCALE = 5,      /* scale is NaN, infinite or negative                 */
+    FA_ERR_ALIGN = 6,      /* a pointer is not 16-byte aligned                   */
+    FA_ERR_FLAG = 7,       /* causal is not 0 or 1                               */
+    FA_ERR_WORKSPACE = 8,  /* workspace NULL, misaligned or too small            */
+    FA_ERR_ALIAS = 9,      /* an output overlaps an input or another output     */
+    FA_ERR_LAUNCH = 10     /* hipGetLastError reported a launch failure          */
+} fa_status;
+
+/*
+ * Forward pass, bf16 inputs and outputs, fp32 accumulation and softmax state.
+ * q [B,Hq,N,d], k and v [B,Hkv,N,d] (bf16, read only); o [B,Hq,N,d] bf16 and
+ * lse [B,Hq,N] fp32 are overwritten.  P is rounded to bf16 (round to nearest
+ * even) before the P.V contraction, and O is rounded to bf16 on store.
+ */
+fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                     hipStream_t stream);
+
+/*
+ * Forward pass with every tensor and every intermediate in fp32 (no reduced
+ * precision anywhere).  Same shapes, layout and rules as fa_forward.
+ */
+fa_status fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                         int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                         hipStream_t stream);
+
+/* Bytes of device workspace fa_backward needs: one fp32 per query row (the
+ * per-row term D_i = sum_t dO_it * O_it).  Returns 0 for invalid sizes. */
+size_t fa_backward_workspace_bytes(int B, int Hq, int N);
+
+/*
+ * Backward pass for L with upstream gradient dO = dL/dO, bf16, recomputing P
+ * tile by tile from the saved lse (the small statistic the forward keeps):
+ *   dP = dO V^T,  D_i = sum_j P_ij dP_ij = dO_i . O_i,  dS = P * (dP - D),
+ *   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
+ * q, k, v, o, dO (bf16) and lse (fp32) are the forward's inputs and outputs.
+ * dq [B,Hq,N,d] and dk, dv [B,Hkv,N,d] (bf16) are overwritten (not accumulated);
+ * dk and dv of a KV head are the sums over the Hq/Hkv query heads of its group.
+ * workspace: device memory of at least fa_backward_workspace_bytes(B,Hq,N)
+ * bytes (passed in workspace_bytes), 16-byte aligned, clobbered by the call.
+ */
+fa_status fa_backward(const void* q, const void* k, const void* v, const void* o,
+                      const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes,
+                      int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                      hipStream_t stream);
+
+/*
+ * Host-only validation of a forward call, exactly as fa_forward performs it
+ * (pointer presence, alignment and overlap, shapes, flag, scale), for an
+ * element size elt_bytes of 2 (bf16) or 4 (fp32).  Touches no device memory
+ * and launches nothing; usable without a GPU.
+ */
+fa_status fa_check_args(const void* q, const void* k, const void* v, const void* o,
+                        const void* lse, int B, int Hq, int Hkv, int N, int d, int causal,
+                        float scale, int elt_bytes);
+
+/* Static, human-readable description of a status code. */
+const char* fa_status_string(fa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,103 @@
+"""The C-ABI library loads, exports what include/fa.h declares, and validates
+arguments on the host (no GPU needed: nothing here launches a kernel)."""
+import ctypes
+import math
+import re
+from pathlib import Path
+
+import pytest
+
+from exact_io_aware_20_amd import api
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "fa.h"
+
+pytestmark = pytest.mark.skipif(not api.LIB_PATH.exists(),
+                                reason="libfa_mi355x.so not built (python -m exact_io_aware_20_amd.build)")
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_entry_points():
+    assert declared_functions() == sorted(api.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(str(api.LIB_PATH))
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = api.load_library()
+    for code, name in api.FA_STATUS.items():
+        s = lib.fa_status_string(code).decode()
+        assert s and s != "unknown status", name
+    assert lib.fa_status_string(99).decode() == "unknown status"
+
+
+def test_workspace_bytes():
+    lib = api.load_library()
+    assert lib.fa_backward_workspace_bytes(2, 32, 8192) == 4 * 2 * 32 * 8192
+    assert lib.fa_backward_workspace_bytes(0, 1, 1) == 0
+    assert lib.fa_backward_workspace_bytes(1, 1, -5) == 0
+
+
+# Fake, never-dereferenced device addresses, 1 GiB apart and 256-byte aligned.
+Q, K, V, O, L = (0x10_0000_0000 + i * (1 << 30) for i in range(5))
+
+
+def check(q=Q, k=K, v=V, o=O, lse=L, B=2, Hq=4, Hkv=2, N=100, d=64, causal=1, scale=0.125, elt=2):
+    return api.load_library().fa_check_args(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, elt)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    ({}, 0),
+    ({"elt": 4, "d": 128}, 0),
+    ({"causal": 0}, 0),
+    ({"scale": 0.0}, 0),
+    ({"q": None}, 1), ({"k": None}, 1), ({"v": None}, 1), ({"o": None}, 1), ({"lse": None}, 1),
+    ({"B": 0}, 2), ({"Hq": 0}, 2), ({"Hkv": 0}, 2), ({"N": 0}, 2), ({"N": -3}, 2), ({"elt": 3}, 2),
+    ({"Hq": 6, "Hkv": 4}, 3),
+    ({"d": 96}, 4), ({"d": 256}, 4), ({"d": 0}, 4),
+    ({"scale": float("nan")}, 5), ({"scale": float("inf")}, 5), ({"scale": -1.0}, 5),
+    ({"q": Q + 8}, 6), ({"o": O + 2}, 6), ({"lse": L + 4}, 6),
+    ({"causal": 2}, 7), ({"causal": -1}, 7),
+    ({"o": Q}, 9), ({"o": K + 64}, 9), ({"lse": O + 16}, 9), ({"lse": V}, 9),
+    ({"B": 1 << 20, "Hq": 1 << 10, "Hkv": 1 << 10, "N": 1 << 16}, 2),
+])
+def test_check_args_codes(kwargs, code):
+    assert check(**kwargs) == code
+
+
+def test_forward_rejects_before_launch():
+    # Invalid calls return their code without touching the GPU.
+    lib = api.load_library()
+    assert lib.fa_forward(None, K, V, O, L, 1, 1, 1, 8, 64, 0, 0.1, None) == 1
+    assert lib.fa_forward(Q, K, V, O, L, 1, 1, 1, 8, 80, 0, 0.1, None) == 4
+    assert lib.fa_forward_f32(Q, K, V, O, L, 1, 3, 2, 8, 64, 0, 0.1, None) == 3
+
+
+def test_backward_rejects_before_launch():
+    lib = api.load_library()
+    base = [Q, K, V, O, 0x20_0000_0000, L, 0x30_0000_0000, 0x40_0000_0000, 0x50_0000_0000]
+    ws = 0x60_0000_0000
+    args = lambda ptrs, ws_, wsb, **kw: lib.fa_backward(
+        *ptrs, ws_, wsb, kw.get("B", 1), kw.get("Hq", 2), kw.get("Hkv", 1), kw.get("N", 16),
+        kw.get("d", 64), kw.get("causal", 1), kw.get("scale", 0.125), None)
+    need = lib.fa_backward_workspace_bytes(1, 2, 16)
+    assert args(base, None, need) == 8
+    assert args(base, ws, need - 4) == 8
+    assert args(base, ws + 4, need) == 8
+    assert args([None] + base[1:], ws, need) == 1
+    assert args(base, ws, need, d=32) == 4
+    bad = list(base)
+    bad[6] = base[0]  # dq aliases q
+    assert args(bad, ws, need) == 9
+    bad = list(base)
+    bad[8] = base[7]  # dv aliases dk
+    assert args(bad, ws, need) == 9
+    assert args(base, base[0], need) == 9  # workspace aliases q
