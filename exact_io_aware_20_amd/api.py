@@ -20,6 +20,7 @@ FA_STATUS = {
     9: "FA_ERR_ALIAS", 10: "FA_ERR_LAUNCH",
 }
 ENTRY_POINTS = ("fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_workspace_bytes",
+                "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq",
                 "fa_check_args", "fa_status_string")
 
 _lib = None
@@ -46,6 +47,12 @@ def load_library() -> ctypes.CDLL:
     lib.fa_forward_f32.restype = i
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
     lib.fa_backward.restype = i
+    lib.fa_backward_preprocess.argtypes = [vp, vp, vp, sz, i, i, i, i, vp]
+    lib.fa_backward_preprocess.restype = i
+    lib.fa_backward_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_backward_dkdv.restype = i
+    lib.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_backward_dq.restype = i
     lib.fa_backward_workspace_bytes.argtypes = [i, i, i]
     lib.fa_backward_workspace_bytes.restype = sz
     lib.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i]
@@ -140,3 +147,31 @@ def backward(q, k, v, o, do, lse, causal: bool, scale: float, dq=None, dk=None, 
                            B, Hq, Hkv, N, d, int(causal), float(scale), _stream(stream))
     _check("fa_backward", code)
     return dq, dk, dv
+
+
+def backward_steps(q, k, v, o, do, lse, causal: bool, scale: float, dq, dk, dv, workspace,
+                   stream=None, steps=("pre", "dkdv", "dq")):
+    """Enqueue the named backward steps (fa_backward_preprocess / _dkdv / _dq) in order.
+
+    Preallocated outputs and workspace are required; this is the form the benchmark
+    uses to time each kernel on its own.
+    """
+    lib = load_library()
+    B, Hq, Hkv, N, d = _shape(q, k)
+    st = _stream(stream)
+    wsb = workspace.numel() * workspace.element_size()
+    for step in steps:
+        if step == "pre":
+            code = lib.fa_backward_preprocess(o.data_ptr(), do.data_ptr(), workspace.data_ptr(), wsb,
+                                              B, Hq, N, d, st)
+        elif step == "dkdv":
+            code = lib.fa_backward_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                                        workspace.data_ptr(), wsb, dk.data_ptr(), dv.data_ptr(),
+                                        B, Hq, Hkv, N, d, int(causal), float(scale), st)
+        elif step == "dq":
+            code = lib.fa_backward_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                                      workspace.data_ptr(), wsb, dq.data_ptr(),
+                                      B, Hq, Hkv, N, d, int(causal), float(scale), st)
+        else:
+            raise ValueError(step)
+        _check(f"fa_backward_{step}", code)

@@ -11,13 +11,12 @@ namespace {
 
 constexpr long long kMaxGrid = 0x7fffffffLL;
 
-struct Range {
-    uintptr_t lo, hi;  // [lo, hi)
-};
-
-bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
-
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t workspace_bytes(int B, int Hq, int N) {
+    if (B < 1 || Hq < 1 || N < 1) return 0;
+    return (size_t)B * Hq * N * sizeof(float);
+}
 
 fa_status check_shape(int B, int Hq, int Hkv, int N, int d, int causal, float scale) {
     if (B < 1 || Hq < 1 || Hkv < 1 || N < 1) return FA_ERR_SHAPE;
@@ -28,32 +27,79 @@ fa_status check_shape(int B, int Hq, int Hkv, int N, int d, int causal, float sc
     return FA_OK;
 }
 
-// Ranges of the forward's tensors; outputs (o, lse) must not overlap anything.
-fa_status check_fwd(const void* q, const void* k, const void* v, const void* o, const void* lse,
-                    int B, int Hq, int Hkv, int N, int d, int causal, float scale, int elt) {
+// One tensor argument: address, byte size, written (output) or only read.
+struct Arg {
+    const void* ptr;
+    uintptr_t bytes;
+    bool out;
+};
+
+// Null, alignment and overlap checks; an output may overlap no other argument.
+fa_status check_tensors(const Arg* a, int n) {
+    for (int i = 0; i < n; ++i)
+        if (!a[i].ptr) return FA_ERR_NULL;
+    for (int i = 0; i < n; ++i)
+        if (!aligned16(a[i].ptr)) return FA_ERR_ALIGN;
+    for (int i = 0; i < n; ++i) {
+        if (!a[i].out) continue;
+        const uintptr_t lo = (uintptr_t)a[i].ptr, hi = lo + a[i].bytes;
+        for (int j = 0; j < n; ++j) {
+            if (j == i) continue;
+            const uintptr_t lo2 = (uintptr_t)a[j].ptr, hi2 = lo2 + a[j].bytes;
+            if (lo < hi2 && lo2 < hi) return FA_ERR_ALIAS;
+        }
+    }
+    return FA_OK;
+}
+
+fa_status check_fwd(const void* q, const void* k, const void* v, const void* o, const void* lse, int B,
+                    int Hq, int Hkv, int N, int d, int causal, float scale, int elt) {
+    if (elt != 2 && elt != 4) return FA_ERR_SHAPE;
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     fa_status s = check_shape(B, Hq, Hkv, N, d, causal, scale);
     if (s != FA_OK) return s;
     const long long grid = elt == 2 ? fa::fwd_bf16_grid(B, Hq, N, d) : fa::fwd_f32_grid(B, Hq, N);
     if (grid > kMaxGrid) return FA_ERR_SHAPE;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-        return FA_ERR_ALIGN;
     const uintptr_t qb = (uintptr_t)B * Hq * N * d * elt, kb = (uintptr_t)B * Hkv * N * d * elt;
-    const uintptr_t lb = (uintptr_t)B * Hq * N * 4;
-    const Range rq{(uintptr_t)q, (uintptr_t)q + qb}, rk{(uintptr_t)k, (uintptr_t)k + kb},
-        rv{(uintptr_t)v, (uintptr_t)v + kb}, ro{(uintptr_t)o, (uintptr_t)o + qb},
-        rl{(uintptr_t)lse, (uintptr_t)lse + lb};
-    const Range outs[2] = {ro, rl};
-    const Range ins[3] = {rq, rk, rv};
-    for (const Range& a : outs)
-        for (const Range& b : ins)
-            if (overlap(a, b)) return FA_ERR_ALIAS;
-    if (overlap(ro, rl)) return FA_ERR_ALIAS;
-    return FA_OK;
+    const Arg a[5] = {{q, qb, false}, {k, kb, false}, {v, kb, false}, {o, qb, true},
+                      {lse, (uintptr_t)B * Hq * N * 4, true}};
+    return check_tensors(a, 5);
 }
 
-fa::FwdParams fwd_params(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                         int Hq, int Hkv, int N, int causal, float scale) {
+enum BwdStep { kAll, kPre, kDkdv, kDq };
+
+fa_status check_bwd(BwdStep step, const void* q, const void* k, const void* v, const void* o,
+                    const void* dO, const void* lse, const void* dq, const void* dk, const void* dv,
+                    const void* workspace, size_t ws_bytes, int B, int Hq, int Hkv, int N, int d,
+                    int causal, float scale) {
+    fa_status s = check_shape(B, Hq, Hkv, N, d, causal, scale);
+    if (s != FA_OK) return s;
+    if (fa::bwd_grid_max(B, Hq, Hkv, N, d) > kMaxGrid) return FA_ERR_SHAPE;
+    const size_t ws_need = workspace_bytes(B, Hq, N);
+    if (!workspace || !aligned16(workspace) || ws_bytes < ws_need) return FA_ERR_WORKSPACE;
+    const uintptr_t qb = (uintptr_t)B * Hq * N * d * 2, kb = (uintptr_t)B * Hkv * N * d * 2;
+    const uintptr_t lb = (uintptr_t)B * Hq * N * 4;
+    Arg a[11];
+    int n = 0;
+    a[n++] = {dO, qb, false};
+    a[n++] = {workspace, ws_need, step == kAll || step == kPre};
+    if (step == kAll || step == kPre) a[n++] = {o, qb, false};
+    if (step != kPre) {
+        a[n++] = {q, qb, false};
+        a[n++] = {k, kb, false};
+        a[n++] = {v, kb, false};
+        a[n++] = {lse, lb, false};
+    }
+    if (step == kAll || step == kDq) a[n++] = {dq, qb, true};
+    if (step == kAll || step == kDkdv) {
+        a[n++] = {dk, kb, true};
+        a[n++] = {dv, kb, true};
+    }
+    return check_tensors(a, n);
+}
+
+fa::FwdParams fwd_params(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                         int Hkv, int N, int causal, float scale) {
     fa::FwdParams p;
     p.q = q;
     p.k = k;
@@ -70,67 +116,9 @@ fa::FwdParams fwd_params(const void* q, const void* k, const void* v, void* o, f
     return p;
 }
 
-}  // namespace
-
-extern "C" {
-
-fa_status fa_check_args(const void* q, const void* k, const void* v, const void* o, const void* lse,
-                        int B, int Hq, int Hkv, int N, int d, int causal, float scale, int elt_bytes) {
-    if (elt_bytes != 2 && elt_bytes != 4) return FA_ERR_SHAPE;
-    return check_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, elt_bytes);
-}
-
-fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-                     int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
-    fa_status s = fa_check_args(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, 2);
-    if (s != FA_OK) return s;
-    const fa::FwdParams p = fwd_params(q, k, v, o, lse, B, Hq, Hkv, N, causal, scale);
-    return fa::launch_fwd_bf16(p, d, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
-}
-
-fa_status fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
-                         int Hq, int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
-    fa_status s = fa_check_args(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, 4);
-    if (s != FA_OK) return s;
-    const fa::FwdParams p = fwd_params(q, k, v, o, lse, B, Hq, Hkv, N, causal, scale);
-    return fa::launch_fwd_f32(p, d, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
-}
-
-size_t fa_backward_workspace_bytes(int B, int Hq, int N) {
-    if (B < 1 || Hq < 1 || N < 1) return 0;
-    return (size_t)B * Hq * N * sizeof(float);
-}
-
-fa_status fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO,
-                      const float* lse, void* dq, void* dk, void* dv, void* workspace,
-                      size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal,
-                      float scale, hipStream_t stream) {
-    if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
-    fa_status s = check_shape(B, Hq, Hkv, N, d, causal, scale);
-    if (s != FA_OK) return s;
-    if (fa::bwd_grid_max(B, Hq, Hkv, N, d) > kMaxGrid) return FA_ERR_SHAPE;
-    const void* ptrs[9] = {q, k, v, o, dO, lse, dq, dk, dv};
-    for (const void* ptr : ptrs)
-        if (!aligned16(ptr)) return FA_ERR_ALIGN;
-    const size_t ws_need = fa_backward_workspace_bytes(B, Hq, N);
-    if (!workspace || !aligned16(workspace) || workspace_bytes < ws_need) return FA_ERR_WORKSPACE;
-
-    const uintptr_t qb = (uintptr_t)B * Hq * N * d * 2, kb = (uintptr_t)B * Hkv * N * d * 2;
-    const uintptr_t lb = (uintptr_t)B * Hq * N * 4;
-    const Range ins[6] = {{(uintptr_t)q, (uintptr_t)q + qb},   {(uintptr_t)k, (uintptr_t)k + kb},
-                          {(uintptr_t)v, (uintptr_t)v + kb},   {(uintptr_t)o, (uintptr_t)o + qb},
-                          {(uintptr_t)dO, (uintptr_t)dO + qb}, {(uintptr_t)lse, (uintptr_t)lse + lb}};
-    const Range outs[4] = {{(uintptr_t)dq, (uintptr_t)dq + qb},
-                           {(uintptr_t)dk, (uintptr_t)dk + kb},
-                           {(uintptr_t)dv, (uintptr_t)dv + kb},
-                           {(uintptr_t)workspace, (uintptr_t)workspace + ws_need}};
-    for (int i = 0; i < 4; ++i) {
-        for (const Range& r : ins)
-            if (overlap(outs[i], r)) return FA_ERR_ALIAS;
-        for (int j = i + 1; j < 4; ++j)
-            if (overlap(outs[i], outs[j])) return FA_ERR_ALIAS;
-    }
-
+fa::BwdParams bwd_params(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                         const float* lse, void* dq, void* dk, void* dv, const void* workspace, int B,
+                         int Hq, int Hkv, int N, int causal, float scale) {
     fa::BwdParams p;
     p.q = q;
     p.k = k;
@@ -149,7 +137,78 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
     p.causal = causal;
     p.scale = scale;
     p.scale_log2 = scale * 1.4426950408889634f;
-    return fa::launch_bwd_bf16(p, d, stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    return p;
+}
+
+fa_status launched(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_check_args(const void* q, const void* k, const void* v, const void* o, const void* lse, int B,
+                        int Hq, int Hkv, int N, int d, int causal, float scale, int elt_bytes) {
+    return check_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, elt_bytes);
+}
+
+fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                     int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
+    fa_status s = check_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, 2);
+    if (s != FA_OK) return s;
+    return launched(fa::launch_fwd_bf16(fwd_params(q, k, v, o, lse, B, Hq, Hkv, N, causal, scale), d, stream));
+}
+
+fa_status fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
+                         int Hq, int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
+    fa_status s = check_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, 4);
+    if (s != FA_OK) return s;
+    return launched(fa::launch_fwd_f32(fwd_params(q, k, v, o, lse, B, Hq, Hkv, N, causal, scale), d, stream));
+}
+
+size_t fa_backward_workspace_bytes(int B, int Hq, int N) { return workspace_bytes(B, Hq, N); }
+
+fa_status fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                      const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                      int B, int Hq, int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
+    fa_status s = check_bwd(kAll, q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
+                            N, d, causal, scale);
+    if (s != FA_OK) return s;
+    const fa::BwdParams p = bwd_params(q, k, v, o, dO, lse, dq, dk, dv, workspace, B, Hq, Hkv, N, causal, scale);
+    if ((s = launched(fa::launch_bwd_pre(p, d, stream))) != FA_OK) return s;
+    if ((s = launched(fa::launch_bwd_dkdv(p, d, stream))) != FA_OK) return s;
+    return launched(fa::launch_bwd_dq(p, d, stream));
+}
+
+fa_status fa_backward_preprocess(const void* o, const void* dO, void* workspace, size_t workspace_bytes, int B,
+                                 int Hq, int N, int d, hipStream_t stream) {
+    fa_status s = check_bwd(kPre, nullptr, nullptr, nullptr, o, dO, nullptr, nullptr, nullptr, nullptr,
+                            workspace, workspace_bytes, B, Hq, Hq, N, d, 0, 1.f);
+    if (s != FA_OK) return s;
+    const fa::BwdParams p = bwd_params(nullptr, nullptr, nullptr, o, dO, nullptr, nullptr, nullptr, nullptr,
+                                       workspace, B, Hq, Hq, N, 0, 1.f);
+    return launched(fa::launch_bwd_pre(p, d, stream));
+}
+
+fa_status fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                           const void* workspace, size_t workspace_bytes, void* dk, void* dv, int B, int Hq,
+                           int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
+    fa_status s = check_bwd(kDkdv, q, k, v, nullptr, dO, lse, nullptr, dk, dv, workspace, workspace_bytes, B,
+                            Hq, Hkv, N, d, causal, scale);
+    if (s != FA_OK) return s;
+    const fa::BwdParams p =
+        bwd_params(q, k, v, nullptr, dO, lse, nullptr, dk, dv, workspace, B, Hq, Hkv, N, causal, scale);
+    return launched(fa::launch_bwd_dkdv(p, d, stream));
+}
+
+fa_status fa_backward_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
+                         const void* workspace, size_t workspace_bytes, void* dq, int B, int Hq, int Hkv, int N,
+                         int d, int causal, float scale, hipStream_t stream) {
+    fa_status s = check_bwd(kDq, q, k, v, nullptr, dO, lse, dq, nullptr, nullptr, workspace, workspace_bytes, B,
+                            Hq, Hkv, N, d, causal, scale);
+    if (s != FA_OK) return s;
+    const fa::BwdParams p =
+        bwd_params(q, k, v, nullptr, dO, lse, dq, nullptr, nullptr, workspace, B, Hq, Hkv, N, causal, scale);
+    return launched(fa::launch_bwd_dq(p, d, stream));
 }
 
 const char* fa_status_string(fa_status status) {

@@ -417,25 +417,37 @@ long long bwd_grid_max(int B, int Hq, int Hkv, int N, int d) {
 }
 
 template <int D>
-static hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
+static hipError_t launch_pre(const BwdParams& p, hipStream_t stream) {
     const long long rows = (long long)p.B * p.Hq * p.N;
-    const unsigned pre_blocks = (unsigned)((rows * (D / 8) + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL(fa_bwd_pre_kernel<D>, dim3(pre_blocks), dim3(kThreads), 0, stream,
+    const unsigned blocks = (unsigned)((rows * (D / 8) + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(fa_bwd_pre_kernel<D>, dim3(blocks), dim3(kThreads), 0, stream,
                        (const uint16_t*)p.o, (const uint16_t*)p.dO, p.dsum, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const unsigned kv_blocks = (unsigned)((long long)p.B * p.Hkv * ((p.N + DkdvCfg<D>::BK - 1) / DkdvCfg<D>::BK));
-    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<D>, dim3(kv_blocks), dim3(kThreads), 0, stream, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    constexpr int br = DqCfg<D, kDqQB>::BR;
-    const unsigned q_blocks = (unsigned)((long long)p.B * p.Hq * ((p.N + br - 1) / br));
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, kDqQB>), dim3(q_blocks), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_bf16(const BwdParams& p, int d, hipStream_t stream) {
-    return d == 64 ? launch_bwd<64>(p, stream) : launch_bwd<128>(p, stream);
+template <int D>
+static hipError_t launch_dkdv(const BwdParams& p, hipStream_t stream) {
+    const unsigned blocks = (unsigned)((long long)p.B * p.Hkv * ((p.N + DkdvCfg<D>::BK - 1) / DkdvCfg<D>::BK));
+    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<D>, dim3(blocks), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_dq(const BwdParams& p, hipStream_t stream) {
+    constexpr int br = DqCfg<D, kDqQB>::BR;
+    const unsigned blocks = (unsigned)((long long)p.B * p.Hq * ((p.N + br - 1) / br));
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, kDqQB>), dim3(blocks), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_pre(const BwdParams& p, int d, hipStream_t stream) {
+    return d == 64 ? launch_pre<64>(p, stream) : launch_pre<128>(p, stream);
+}
+hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t stream) {
+    return d == 64 ? launch_dkdv<64>(p, stream) : launch_dkdv<128>(p, stream);
+}
+hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t stream) {
+    return d == 64 ? launch_dq<64>(p, stream) : launch_dq<128>(p, stream);
 }
 
 }  // namespace fa

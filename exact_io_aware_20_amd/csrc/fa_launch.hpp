@@ -42,6 +42,8 @@ long long bwd_grid_max(int B, int Hq, int Hkv, int N, int d);
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t stream);
-hipError_t launch_bwd_bf16(const BwdParams& p, int d, hipStream_t stream);
+hipError_t launch_bwd_pre(const BwdParams& p, int d, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t stream);
 
 }  // namespace fa

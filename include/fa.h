@@ -102,6 +102,26 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
                       hipStream_t stream);
 
 /*
+ * The three steps fa_backward enqueues, in this order, exposed so that a caller
+ * can place them itself (after fa_backward_preprocess, fa_backward_dkdv and
+ * fa_backward_dq only read the workspace and may run concurrently on two
+ * streams).  Arguments, layouts and errors are those of fa_backward.
+ *   fa_backward_preprocess: workspace[row] = D_row = sum_t dO_row,t * O_row,t (fp32).
+ *   fa_backward_dkdv: dk, dv from q, k, v, dO, lse and the preprocessed workspace.
+ *   fa_backward_dq:   dq from q, k, v, dO, lse and the preprocessed workspace.
+ */
+fa_status fa_backward_preprocess(const void* o, const void* dO, void* workspace, size_t workspace_bytes,
+                                 int B, int Hq, int N, int d, hipStream_t stream);
+fa_status fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                           const float* lse, const void* workspace, size_t workspace_bytes,
+                           void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal,
+                           float scale, hipStream_t stream);
+fa_status fa_backward_dq(const void* q, const void* k, const void* v, const void* dO,
+                         const float* lse, const void* workspace, size_t workspace_bytes,
+                         void* dq, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                         hipStream_t stream);
+
+/*
  * Host-only validation of a forward call, exactly as fa_forward performs it
  * (pointer presence, alignment and overlap, shapes, flag, scale), for an
  * element size elt_bytes of 2 (bf16) or 4 (fp32).  Touches no device memory

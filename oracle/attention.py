@@ -41,6 +41,8 @@ blocked, fused or reordered beyond what a BLAS matmul does internally.
 """
 from __future__ import annotations
 
+import contextlib
+import multiprocessing
 import os
 from concurrent.futures import ProcessPoolExecutor
 
@@ -157,12 +159,29 @@ def _bwd_unit(args):
     return head_backward(q, k, v, do, causal, scale)
 
 
+@contextlib.contextmanager
 def _pool(workers: int):
-    # One BLAS thread per worker process; the environment is inherited by the
-    # workers, which load their BLAS after this point.
-    os.environ.setdefault("OPENBLAS_NUM_THREADS", "1")
-    os.environ.setdefault("OMP_NUM_THREADS", "1")
-    return ProcessPoolExecutor(max_workers=workers)
+    """Process pool of fresh interpreters (spawn), one BLAS thread each."""
+    keys = ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS", "MKL_NUM_THREADS")
+    saved = {k: os.environ.get(k) for k in keys}
+    os.environ.update({k: "1" for k in keys})
+    try:
+        with ProcessPoolExecutor(max_workers=workers,
+                                 mp_context=multiprocessing.get_context("spawn")) as ex:
+            yield ex
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def _run(fn, jobs, workers: int):
+    if workers > 1 and len(jobs) > 1:
+        with _pool(min(workers, len(jobs))) as ex:
+            return list(ex.map(fn, jobs))
+    return [fn(j) for j in jobs]
 
 
 def attention_forward(q, k, v, causal: bool, scale: float, heads=None, rows=None, workers: int = 1):
@@ -181,11 +200,7 @@ def attention_forward(q, k, v, causal: bool, scale: float, heads=None, rows=None
     lse = np.full(q.shape[:3], np.nan)
     jobs = [(q[b, h], k[b, _group(h, hq_, hkv_)], v[b, _group(h, hq_, hkv_)], causal, scale, rows)
             for b, h in heads]
-    if workers > 1 and len(jobs) > 1:
-        with _pool(workers) as ex:
-            results = list(ex.map(_fwd_unit, jobs))
-    else:
-        results = [_fwd_unit(j) for j in jobs]
+    results = _run(_fwd_unit, jobs, workers)
     sel = slice(None) if rows is None else np.asarray(rows)
     for (b, h), (ob, lb) in zip(heads, results):
         o[b, h, sel] = ob
@@ -210,11 +225,7 @@ def attention_backward(q, k, v, do, causal: bool, scale: float, groups=None, wor
     dv = np.full(v.shape, np.nan)
     units = [(b, hk, h) for b, hk in groups for h in range(hk * g, hk * g + g)]
     jobs = [(q[b, h], k[b, hk], v[b, hk], do[b, h], causal, scale) for b, hk, h in units]
-    if workers > 1 and len(jobs) > 1:
-        with _pool(workers) as ex:
-            results = list(ex.map(_bwd_unit, jobs))
-    else:
-        results = [_bwd_unit(j) for j in jobs]
+    results = _run(_bwd_unit, jobs, workers)
     for b, hk in groups:
         dk[b, hk] = 0.0
         dv[b, hk] = 0.0
