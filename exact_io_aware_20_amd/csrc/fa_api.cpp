@@ -98,6 +98,16 @@ fa_status check_bwd(BwdStep step, const void* q, const void* k, const void* v, c
     return check_tensors(a, n);
 }
 
+// scale * log2(e) as the kernels use it.  The kernels mask a score by setting it
+// to -inf and rely on -inf * scale_log2 = -inf (p = exp2(-inf) = 0); for scale = 0
+// the smallest normal float is used instead: any score below 2^60 in magnitude
+// times it is below 2^-66, so exp2 of it rounds to exactly 1.0, as exp(0 * s) is;
+// LSE and the gradients (which use `scale` itself) are unchanged.
+float kernel_scale_log2(float scale) {
+    const float s = scale * 1.4426950408889634f;
+    return s > 0.f ? s : 1.17549435e-38f;
+}
+
 fa::FwdParams fwd_params(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                          int Hkv, int N, int causal, float scale) {
     fa::FwdParams p;
@@ -112,7 +122,7 @@ fa::FwdParams fwd_params(const void* q, const void* k, const void* v, void* o, f
     p.N = N;
     p.causal = causal;
     p.scale = scale;
-    p.scale_log2 = scale * 1.4426950408889634f;
+    p.scale_log2 = kernel_scale_log2(scale);
     return p;
 }
 
@@ -136,7 +146,7 @@ fa::BwdParams bwd_params(const void* q, const void* k, const void* v, const void
     p.N = N;
     p.causal = causal;
     p.scale = scale;
-    p.scale_log2 = scale * 1.4426950408889634f;
+    p.scale_log2 = kernel_scale_log2(scale);
     return p;
 }
 

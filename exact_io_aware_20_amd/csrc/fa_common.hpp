@@ -175,4 +175,171 @@ __device__ __forceinline__ u32x4 frag_transposed(const uint16_t* base, int col, 
     return cat(lds8(p), lds8(p + 8));
 }
 
+
+// ---------------------------------------------------------------------------------
+// Swizzled natural tile [64][D] in LDS, filled by direct global->LDS loads
+// (global_load_lds_dwordx4: lane L of a wave writes 16 bytes at base + 16*L).
+// Row r's 16-byte chunk j lives at slot j ^ swz(r), with no padding; the swizzle
+// spreads the 32 rows a fragment read touches over all 64 LDS banks.
+// ---------------------------------------------------------------------------------
+template <int D, int MODE = 0>
+struct SwzTile {
+    static constexpr int CHUNKS = D / 8;          // 16-byte chunks per row
+    static constexpr int ELEMS = 64 * D;          // bf16 elements per tile
+    static constexpr int WAVE_LOADS = 64 * CHUNKS / kWave;   // wave-instructions per tile
+    // MODE 0 spreads 32 consecutive rows (fragment reads), MODE 1 spreads rows
+    // 4k + j for k = 0..15 (the transposing reads of permt_from_lds).
+    __device__ static __forceinline__ int swz(int r) {
+        if (MODE == 0) return D == 128 ? (r & 15) : ((r >> 1) & 7);
+        return D == 128 ? ((r >> 2) & 15) : ((r >> 2) & 7);
+    }
+    // element offset of (row, chunk)
+    __device__ static __forceinline__ int at(int r, int j) { return r * D + ((j ^ swz(r)) << 3); }
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Returns x unchanged, but opaque to the optimiser: per-lane address arithmetic
+// that depends on it is recomputed where it is used instead of being hoisted out
+// of the main loop and kept live (which would spill under full register use).
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// Issue the direct loads of one 64-row tile: wave-instruction i (of WAVE_LOADS)
+// covers LDS chunk positions [64 i, 64 i + 64).  Rows at or past `nvalid` are
+// read from row nvalid-1 instead (always in bounds; callers mask those rows or
+// give them zero weight).
+template <int D, int MODE = 0>
+__device__ __forceinline__ int swz_tile_issue(const uint16_t* src, int nvalid, uint16_t* lds_tile,
+                                              int wave, int nwaves, int lane) {
+    using S = SwzTile<D, MODE>;
+    lane = opaque(lane);
+    int issued = 0;
+#pragma unroll
+    for (int k = 0; k < (S::WAVE_LOADS + 7) / 8; ++k) {
+        const int i = wave + k * nwaves;
+        if (i < S::WAVE_LOADS) {
+            const int pos = i * 64 + lane;
+            const int r = pos / S::CHUNKS;
+            const int slot = pos % S::CHUNKS;
+            const int j = slot ^ S::swz(r);
+            const int rr = r < nvalid ? r : nvalid - 1;
+            __builtin_amdgcn_global_load_lds(src + (size_t)rr * D + j * 8,
+                                             (lds_void*)(lds_tile + i * 64 * 8), 16, 0, 0);
+            ++issued;
+        }
+    }
+    return issued;
+}
+
+// ---------------------------------------------------------------------------------
+// Padded natural tile [64][D + 8] in LDS, filled by direct loads: each 16-byte
+// slot of a row (D/8 data chunks plus one pad slot) is one lane of a direct load,
+// so a tile is SLOTS wave-instructions.  Rows are 16 bytes longer than the data
+// (a 4-bank shift per row: the 32 rows of a fragment read hit distinct banks),
+// and fragment addresses are a per-lane base plus compile-time offsets.
+// ---------------------------------------------------------------------------------
+template <int D>
+struct PadTile {
+    static constexpr int STR = D + 8;                 // row stride, elements
+    static constexpr int SLOTS = D / 8 + 1;           // 16-byte slots per row
+    static constexpr int ELEMS = 64 * STR;
+    static constexpr int WAVE_LOADS = SLOTS;          // 64 rows x SLOTS / 64 lanes
+    __device__ static __forceinline__ int at(int r, int j) { return r * STR + j * 8; }
+};
+
+template <int D>
+__device__ __forceinline__ int pad_tile_issue(const uint16_t* src, int nvalid, uint16_t* lds_tile, int wave,
+                                              int nwaves, int lane) {
+    using P = PadTile<D>;
+    lane = opaque(lane);
+    int issued = 0;
+#pragma unroll
+    for (int k = 0; k < (P::WAVE_LOADS + 7) / 8; ++k) {
+        const int i = wave + k * nwaves;
+        if (i < P::WAVE_LOADS) {
+            const int pos = i * 64 + lane;
+            const int r = pos / P::SLOTS;
+            const int j = pos % P::SLOTS;
+            const int rr = r < nvalid ? r : nvalid - 1;
+            // the pad slot reloads chunk 0 of its row: in bounds, never read
+            const int jj = j < P::SLOTS - 1 ? j : 0;
+            __builtin_amdgcn_global_load_lds(src + (size_t)rr * D + jj * 8,
+                                             (lds_void*)(lds_tile + i * 64 * 8), 16, 0, 0);
+            ++issued;
+        }
+    }
+    return issued;
+}
+
+// ---------------------------------------------------------------------------------
+// Transposed tile with key-permuted columns: [D][64 + 8] bf16.  Column position of
+// key k within its 16-key block: 8*((k/4)&1) + 4*((k/8)&1) + (k%4), so that the 8
+// keys one lane feeds to a 32x32x16 MFMA (k-slot order 4h+{0..3}, 8+4h+{0..3}) are
+// contiguous and a fragment is one 16-byte read.
+// ---------------------------------------------------------------------------------
+template <int D>
+struct PermT {
+    static constexpr int STR = 64 + 8;
+    static constexpr int ELEMS = D * STR;
+    static constexpr int ITEMS = (D / 8) * 16;   // 4 keys x 8 columns per item
+};
+
+__device__ __forceinline__ int perm_pos4(int kq) {   // position of key 4*kq
+    return 16 * (kq >> 2) + 8 * (kq & 1) + 4 * ((kq >> 1) & 1);
+}
+
+// Items are numbered key-quad fastest: the 16 lanes of a store cover one row's 64
+// keys, so a wave's eight-byte stores hit distinct banks.
+template <int D>
+__device__ __forceinline__ void permt_load(u32x4 (&r)[4], const uint16_t* src, int nvalid, int item) {
+    const int kq = item % 16, c = item / 16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = kq * 4 + j;
+        r[j] = row < nvalid ? ld_global16(src + (size_t)row * D + c * 8) : zero_u4();
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void permt_store(const u32x4 (&r)[4], uint16_t* dst, int item) {
+    const int kq = item % 16, c = item / 16;
+    const int col = perm_pos4(kq);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const uint32_t a = r[0][w], b = r[1][w], cc = r[2][w], d = r[3][w];
+        const u32x2 even = {(a & 0xffffu) | (b << 16), (cc & 0xffffu) | (d << 16)};
+        const u32x2 odd = {(a >> 16) | (b & 0xffff0000u), (cc >> 16) | (d & 0xffff0000u)};
+        *(u32x2*)(dst + (c * 8 + 2 * w) * PermT<D>::STR + col) = even;
+        *(u32x2*)(dst + (c * 8 + 2 * w + 1) * PermT<D>::STR + col) = odd;
+    }
+}
+
+// Transpose one item (4 keys x 8 columns) from a MODE 1 swizzled natural tile in
+// LDS into the permuted transposed layout.  Rows >= nvalid are written as zero, so
+// stale or clamped rows contribute nothing to P.V.
+template <int D>
+__device__ __forceinline__ void permt_from_lds(const uint16_t* src, uint16_t* dst, int nvalid, int item) {
+    using S = SwzTile<D, 1>;
+    item = opaque(item);
+    const int kq = item % 16, c = item / 16;
+    u32x4 r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = kq * 4 + j;
+        r[j] = lds16(src + S::at(row, c));
+        if (row >= nvalid) r[j] = zero_u4();
+    }
+    permt_store<D>(r, dst, item);
+}
+
+// Fragment of the permuted transposed tile: row `row` (an index into d), the 8
+// keys kk + {4h..4h+3, 8+4h..8+4h+3} (kk a multiple of 16).
+template <int D>
+__device__ __forceinline__ u32x4 permt_frag(const uint16_t* base, int row, int kk, int half) {
+    return lds16(base + row * PermT<D>::STR + kk + 8 * half);
+}
+
 }  // namespace fa

@@ -10,8 +10,11 @@
 // summary, "GPU 显存和注意力瓶颈": a token sees itself and earlier tokens).
 //
 // gfx950 mapping of the bf16 kernel:
-//   * 4 waves per workgroup, each wave owns 32*QB query rows; K/V tiles of 64
-//     keys are staged through LDS (double-buffered, one barrier per tile).
+//   * 8 waves per workgroup (two per SIMD, so one wave's softmax overlaps the
+//     other's matrix work), each owning 32 query rows.  K/V tiles of 64 keys are
+//     double-buffered in LDS with one barrier per tile: K arrives by direct
+//     global->LDS loads into an XOR-swizzled layout, V through registers into a
+//     transposed, key-permuted layout whose fragments are single 16-byte reads.
 //   * Scores are formed transposed, S^T = K Q^T, so a lane holds one query (its
 //     column) and 16 keys; the row maximum is an in-lane max plus one exchange
 //     with lane l^32, and the running statistics are lane-local scalars.
@@ -29,23 +32,122 @@ namespace fa {
 
 constexpr float kRescaleLog2 = 8.0f;
 
-template <int D, int QB>
+template <int D>
 struct FwdCfg {
-    static constexpr int BR = kWaves * 32 * QB;   // query rows per workgroup
+    static constexpr int WAVES = 8;               // two waves per SIMD
+    static constexpr int THREADS = WAVES * kWave;
+    static constexpr int BR = WAVES * 32;         // query rows per workgroup (32 per wave)
     static constexpr int BC = 64;                 // keys per K/V tile
     static constexpr int DC = D / 16;             // k-chunks of the S contraction
     static constexpr int DB = D / 32;             // 32-row blocks of O^T
-    using T = Tile64<D>;
-    static constexpr int K_OFF = 0;
-    static constexpr int V_OFF = T::N_ELEMS;
-    static constexpr int STAGE = T::N_ELEMS + T::T_ELEMS;
 };
 
-template <int D, int QB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// S^T = K Q^T for one 64-key tile and one wave's 32 queries: two 32 x 32 blocks,
+// each a chain of D/16 MFMAs.  All K fragments of a 16-wide chunk pair are read
+// before their MFMAs so that LDS latency overlaps the matrix pipe.
+template <int D>
+__device__ __forceinline__ void fwd_scores(const uint16_t* Ks, const u32x4 (&qf)[D / 16], f32x16 (&s)[2],
+                                           int l32, int hh) {
+    using KT = SwzTile<D, 0>;
+    s[0] = zero16();
+    s[1] = zero16();
+    constexpr int G = D / 32;   // groups of two k-chunks
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        u32x4 kf[2][2];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) kf[cc][kb] = lds16(Ks + KT::at(32 * kb + l32, 2 * (2 * g + cc) + hh));
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(kf[cc][kb], qf[2 * g + cc], s[kb]);
+    }
+}
+
+// Max over the wave's lane pair (l, l^32) that share a query column.
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Online-softmax update of one tile's scores and O^T += V^T P^T.  `mask`
+// (wave-uniform) applies the causal diagonal and keys >= N.
+template <int D>
+__device__ __forceinline__ void fwd_softmax_pv(f32x16 (&s)[2], const uint16_t* Vt, f32x16 (&o)[D / 32],
+                                               float& m_ref, float& l_part, float sl2, int k0, int q, int N,
+                                               int causal, int l32, int hh, bool mask) {
+    if (mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const bool vis = key < N && (!causal || key <= q);
+                s[kb][r] = vis ? s[kb][r] : kNegInf;
+            }
+    }
+    // row max: in-lane max3 chain, then the partner lane; lazy rescale
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = pair_max(mx);
+    const float mt = mx * sl2;   // sl2 > 0, so -inf stays -inf
+    const bool need = mt > m_ref + kRescaleLog2;
+    if (__ballot(need)) {
+        const float mnew = need ? mt : m_ref;
+        const float alpha = m_ref == kNegInf ? 0.f : fast_exp2(m_ref - mnew);
+        m_ref = mnew;
+        l_part *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    // P = 2^(S*sl2 - m) (masked scores are -inf: p = 0), packed to bf16 as the
+    // B operand of O^T = V^T P^T; l accumulates the same rounded values
+    const float mref = m_ref == kNegInf ? 0.f : m_ref;
+    u32x4 pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float pa = fast_exp2(__builtin_fmaf(s[kb][8 * h2 + 2 * j], sl2, -mref));
+                const float pb = fast_exp2(__builtin_fmaf(s[kb][8 * h2 + 2 * j + 1], sl2, -mref));
+                const uint32_t pk = pack_bf16(pa, pb);
+                pf[kb][h2][j] = pk;
+                l_part = add_bf16_pair(pk, l_part);
+            }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const u32x4 vf = permt_frag<D>(Vt, 32 * db + l32, 32 * kb + 16 * h2, hh);
+                o[db] = mfma32x32x16(vf, pf[kb][h2], o[db]);
+            }
+}
+
+// The kernel is software-pipelined by one tile: S(t+1) = K(t+1) Q^T is issued
+// to the matrix cores before the softmax of tile t, so the two can overlap.  LDS
+// holds K(t+1) and V(t) during iteration t; K(t+2) (direct loads) and V(t+1)
+// (through registers, transposed on the way) are written into the other halves
+// of the two double buffers meanwhile, one workgroup barrier per iteration.
+template <int D>
+__global__ __launch_bounds__(FwdCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_kernel(FwdParams p) {
-    using C = FwdCfg<D, QB>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
+    using C = FwdCfg<D>;
+    constexpr int KB = SwzTile<D, 0>::ELEMS;
+    constexpr int VB = PermT<D>::ELEMS;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * KB + 2 * VB];
+    uint16_t* kbuf = smem;            // K tile of parity t&1 at kbuf + (t&1)*KB
+    uint16_t* vbuf = smem + 2 * KB;   // V tile of parity t&1 at vbuf + (t&1)*VB
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -66,177 +168,80 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     const uint16_t* Vh = (const uint16_t*)p.v + ((size_t)b * p.Hkv + hkv) * N * D;
 
     const int q0 = qt * C::BR;
-    const int qw0 = q0 + wave * 32 * QB;
+    const int qw0 = q0 + wave * 32;
+    const int q = qw0 + l32;
     const int q_last = min(q0 + C::BR, N) - 1;
     const int ntiles = p.causal ? q_last / C::BC + 1 : (N + C::BC - 1) / C::BC;
-    const int wq_last = min(qw0 + 32 * QB, N) - 1;
+    const int wq_last = min(qw0 + 32, N) - 1;
     const int wave_tiles = wq_last < qw0 ? 0 : (p.causal ? wq_last / C::BC + 1 : ntiles);
 
     // Q fragments: B operand of S^T = K Q^T (lane: query, slots: 8 consecutive d).
-    u32x4 qf[QB][C::DC];
+    u32x4 qf[C::DC];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int q = qw0 + 32 * qb + l32;
-#pragma unroll
-        for (int c = 0; c < C::DC; ++c)
-            qf[qb][c] = q < N ? ld_global16(Qh + (size_t)q * D + 16 * c + 8 * hh) : zero_u4();
-    }
+    for (int c = 0; c < C::DC; ++c)
+        qf[c] = q < N ? ld_global16(Qh + (size_t)q * D + 16 * c + 8 * hh) : zero_u4();
 
-    f32x16 o[C::DB][QB];
-    float m_ref[QB], l_part[QB];
+    f32x16 o[C::DB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        m_ref[qb] = kNegInf;
-        l_part[qb] = 0.f;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) o[db][qb] = zero16();
-    }
+    for (int db = 0; db < C::DB; ++db) o[db] = zero16();
+    float m_ref = kNegInf, l_part = 0.f;
     const float sl2 = p.scale_log2;
 
-    TileRegs<D> kr, vr;
-    tile_load<D>(kr, Kh, N, tid);
-    tile_load<D>(vr, Vh, N, tid);
-    tile_store_natural<D>(kr, smem + C::K_OFF, tid);
-    tile_store_transposed<D>(vr, smem + C::V_OFF, tid);
+    // V tile items (4 keys x 8 columns) are staged by the first ITEMS threads.
+    const bool v_stager = tid < PermT<D>::ITEMS;
+    u32x4 vr[4];
+    auto issue_k = [&](int t, uint16_t* buf) {
+        swz_tile_issue<D, 0>(Kh + (size_t)t * C::BC * D, N - t * C::BC, buf, wave, C::WAVES, lane);
+    };
+
+    // prologue: K(0), V(0) -> LDS; S(0); K(1) -> LDS
+    issue_k(0, kbuf);
+    if (v_stager) {
+        permt_load<D>(vr, Vh, N, tid);
+        permt_store<D>(vr, vbuf, tid);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    f32x16 sa[2], sb[2];
+    if (0 < wave_tiles) fwd_scores<D>(kbuf, qf, sa, l32, hh);
+    if (1 < ntiles) issue_k(1, kbuf + KB);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int t = 0; t < ntiles; ++t) {
+    // one pipelined step: tile t's softmax/PV with scores `cur`, tile t+1's scores into `nxt`
+    auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
         const int k0 = t * C::BC;
+        if (t + 2 < ntiles) issue_k(t + 2, kbuf + (t & 1) * KB);
         const bool more = t + 1 < ntiles;
-        if (more) {
-            tile_load<D>(kr, Kh + (size_t)(k0 + C::BC) * D, N - (k0 + C::BC), tid);
-            tile_load<D>(vr, Vh + (size_t)(k0 + C::BC) * D, N - (k0 + C::BC), tid);
-        }
-        const uint16_t* Ks = smem + (t & 1) * C::STAGE + C::K_OFF;
-        const uint16_t* Vt = smem + (t & 1) * C::STAGE + C::V_OFF;
-
+        if (more && v_stager) permt_load<D>(vr, Vh + (size_t)(k0 + C::BC) * D, N - (k0 + C::BC), tid);
+        if (t + 1 < wave_tiles) fwd_scores<D>(kbuf + ((t + 1) & 1) * KB, qf, nxt, l32, hh);
         if (t < wave_tiles) {
-            // ---- S^T = K Q^T : [2 key blocks][QB query blocks] of 32 x 32
-            f32x16 s[2][QB];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) s[kb][qb] = zero16();
-#pragma unroll
-            for (int c = 0; c < C::DC; ++c) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const u32x4 kf = frag_natural<D>(Ks, 32 * kb + l32, c, hh);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma32x32x16(kf, qf[qb][c], s[kb][qb]);
-                }
-            }
-
-            // ---- mask: the causal diagonal and keys past N (ragged last tile)
-            const bool need_mask = (p.causal && k0 + C::BC - 1 > qw0) || (k0 + C::BC > N);
-            if (need_mask) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const int q = qw0 + 32 * qb + l32;
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                            const bool vis = key < N && (!p.causal || key <= q);
-                            s[kb][qb][r] = vis ? s[kb][qb][r] : kNegInf;
-                        }
-                }
-            }
-
-            // ---- online softmax: row max (in-lane + partner lane), lazy rescale
-            float mt[QB];
-            bool need = false;
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                float mx = kNegInf;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                mt[qb] = mx == kNegInf ? kNegInf : mx * sl2;
-                need |= mt[qb] > m_ref[qb] + kRescaleLog2;
-            }
-            if (__ballot(need)) {
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    const float mnew = mt[qb] > m_ref[qb] + kRescaleLog2 ? mt[qb] : m_ref[qb];
-                    const float alpha = m_ref[qb] == kNegInf ? 0.f : fast_exp2(m_ref[qb] - mnew);
-                    m_ref[qb] = mnew;
-                    l_part[qb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) o[db][qb][r] *= alpha;
-                }
-            }
-
-            // ---- P = 2^(S*sl2 - m), packed to bf16 as the B operand of O^T = V^T P^T
-            u32x4 pf[QB][2][2];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const float mref = m_ref[qb] == kNegInf ? 0.f : m_ref[qb];
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const float sa = s[kb][qb][8 * h2 + 2 * j];
-                            const float sb = s[kb][qb][8 * h2 + 2 * j + 1];
-                            float pa = fast_exp2(__builtin_fmaf(sa, sl2, -mref));
-                            float pb = fast_exp2(__builtin_fmaf(sb, sl2, -mref));
-                            if (need_mask) {
-                                pa = sa == kNegInf ? 0.f : pa;
-                                pb = sb == kNegInf ? 0.f : pb;
-                            }
-                            const uint32_t pk = pack_bf16(pa, pb);
-                            pf[qb][kb][h2][j] = pk;
-                            l_part[qb] = add_bf16_pair(pk, l_part[qb]);
-                        }
-            }
-
-            // ---- O^T += V^T P^T
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                    for (int db = 0; db < C::DB; ++db) {
-                        const u32x4 vf = frag_transposed<D>(Vt, 32 * db + l32, 32 * kb + 16 * h2, hh);
-#pragma unroll
-                        for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma32x32x16(vf, pf[qb][kb][h2], o[db][qb]);
-                    }
+            const bool mask = (p.causal && k0 + C::BC - 1 > qw0) || (k0 + C::BC > N);
+            fwd_softmax_pv<D>(cur, vbuf + (t & 1) * VB, o, m_ref, l_part, sl2, k0, q, N, p.causal, l32, hh, mask);
         }
-
-        if (more) {
-            uint16_t* nb = smem + ((t + 1) & 1) * C::STAGE;
-            tile_store_natural<D>(kr, nb + C::K_OFF, tid);
-            tile_store_transposed<D>(vr, nb + C::V_OFF, tid);
-        }
+        if (more && v_stager) permt_store<D>(vr, vbuf + ((t + 1) & 1) * VB, tid);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        step(t, sa, sb);
+        if (t + 1 < ntiles) step(t + 1, sb, sa);
     }
 
     // ---- epilogue: O = O^T / l (bf16, round to nearest even), LSE in natural log
-    uint16_t* Oh = (uint16_t*)p.o + (size_t)head * N * D;
-    float* lse = p.lse + (size_t)head * N;
+    const float lt = l_part + __shfl_xor(l_part, 32);
+    if (q < N) {
+        uint16_t* Oh = (uint16_t*)p.o + (size_t)head * N * D + (size_t)q * D;
+        const float inv = 1.0f / lt;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float lt = l_part[qb] + __shfl_xor(l_part[qb], 32);
-        const int q = qw0 + 32 * qb + l32;
-        if (q < N) {
-            const float inv = 1.0f / lt;
+        for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const u32x2 v2 = {pack_bf16(o[db][qb][4 * g] * inv, o[db][qb][4 * g + 1] * inv),
-                                      pack_bf16(o[db][qb][4 * g + 2] * inv, o[db][qb][4 * g + 3] * inv)};
-                    *(u32x2*)(Oh + (size_t)q * D + 32 * db + 8 * g + 4 * hh) = v2;
-                }
-            if (hh == 0) lse[q] = (m_ref[qb] + __log2f(lt)) * kLn2;
-        }
+            for (int g = 0; g < 4; ++g) {
+                const u32x2 v2 = {pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                                  pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+                *(u32x2*)(Oh + 32 * db + 8 * g + 4 * hh) = v2;
+            }
+        if (hh == 0) p.lse[(size_t)head * N + q] = (m_ref + __log2f(lt)) * kLn2;
     }
 }
 
@@ -325,21 +330,21 @@ __global__ __launch_bounds__(64) void fa_fwd_f32_kernel(FwdParams p) {
 // ---------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------
-template <int D, int QB>
+template <int D>
 static hipError_t launch_bf16(const FwdParams& p, hipStream_t stream) {
-    const int br = FwdCfg<D, QB>::BR;
+    constexpr int br = FwdCfg<D>::BR;
     const long long nblk = (long long)p.B * p.Hq * ((p.N + br - 1) / br);
-    hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, QB>), dim3((unsigned)nblk), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fa_fwd_bf16_kernel<D>), dim3((unsigned)nblk), dim3(FwdCfg<D>::THREADS), 0, stream, p);
     return hipGetLastError();
 }
 
 long long fwd_bf16_grid(int B, int Hq, int N, int d) {
-    const int br = d == 64 ? FwdCfg<64, kFwdQB64>::BR : FwdCfg<128, kFwdQB128>::BR;
+    const int br = d == 64 ? FwdCfg<64>::BR : FwdCfg<128>::BR;
     return (long long)B * Hq * ((N + br - 1) / br);
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t stream) {
-    return d == 64 ? launch_bf16<64, kFwdQB64>(p, stream) : launch_bf16<128, kFwdQB128>(p, stream);
+    return d == 64 ? launch_bf16<64>(p, stream) : launch_bf16<128>(p, stream);
 }
 
 long long fwd_f32_grid(int B, int Hq, int N) { return (long long)B * Hq * ((N + 31) / 32); }

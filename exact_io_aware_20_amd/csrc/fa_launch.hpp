@@ -32,10 +32,6 @@ struct BwdParams {
     float scale_log2;
 };
 
-// Query-row blocks per wave (32 rows each) of the bf16 forward, per head dim.
-constexpr int kFwdQB64 = 2;
-constexpr int kFwdQB128 = 2;
-
 long long fwd_bf16_grid(int B, int Hq, int N, int d);
 long long fwd_f32_grid(int B, int Hq, int N);
 long long bwd_grid_max(int B, int Hq, int Hkv, int N, int d);
