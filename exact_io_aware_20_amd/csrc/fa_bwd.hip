@@ -58,24 +58,88 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_pre_kernel(const uint16_t* o,
 // ---------------------------------------------------------------------------------
 template <int D>
 struct DkdvCfg {
-    static constexpr int BK = kWaves * 32;  // keys per workgroup
+    static constexpr int WAVES = 4;
+    static constexpr int THREADS = WAVES * kWave;
+    static constexpr int BK = WAVES * 32;   // keys per workgroup
     static constexpr int BQ = 64;           // query rows per streamed tile
     static constexpr int DC = D / 16;
     static constexpr int DB = D / 32;
-    using T = Tile64<D>;
-    static constexpr int QN = 0;
-    static constexpr int QT = QN + T::N_ELEMS;
-    static constexpr int GN = QT + T::T_ELEMS;   // dO natural
-    static constexpr int GT = GN + T::N_ELEMS;   // dO transposed
-    static constexpr int VEC = GT + T::T_ELEMS;  // 64 fp32 LSE*log2e, then 64 fp32 D
-    static constexpr int STAGE = VEC + 2 * 64 * 2;
+    static constexpr int NAT = SwzTile<D, 0>::ELEMS;   // natural Q or dO tile
+    static constexpr int TR = PermT<D>::ELEMS;         // transposed Q or dO tile
+    static constexpr int NSTAGE = 2 * NAT;                 // natural Q, dO
+    static constexpr int TSTAGE = 2 * TR + 2 * 64 * 2;     // transposed Q, dO; LSE*log2e, D (fp32)
 };
 
+// Per streamed tile and wave (32 keys x 64 queries in two 32-query halves qb):
+// S = Q K^T and dP = dO V^T with the queries on the C rows.
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__device__ __forceinline__ void dkdv_scores(const uint16_t* qn, const uint16_t* gn, const u32x4 (&kf)[D / 16],
+                                            const u32x4 (&vf)[D / 16], f32x16 (&s)[2], f32x16 (&dp)[2], int l32,
+                                            int hh) {
+    using NT = SwzTile<D, 2>;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        s[qb] = zero16();
+        dp[qb] = zero16();
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+            s[qb] = mfma32x32x16(lds16(qn + NT::at(32 * qb + l32, 2 * c + hh)), kf[c], s[qb]);
+            dp[qb] = mfma32x32x16(lds16(gn + NT::at(32 * qb + l32, 2 * c + hh)), vf[c], dp[qb]);
+        }
+    }
+}
+
+// Then half by half: P = 2^(S*sl2 - LSE2), dS = P (dP - D) on the vector ALU and
+// dV^T += dO^T P, dK^T += Q^T dS on the matrix cores, so that one half's products
+// overlap the other half's vector work.  Queries of register r: 32*qb + 8*(r/4) +
+// 4*hh + r%4.
+template <int D>
+__device__ __forceinline__ void dkdv_grads(const f32x16 (&s)[2], const f32x16 (&dp)[2], const uint16_t* qtr,
+                                           const uint16_t* gtr, const float* lse2, const float* dvec,
+                                           f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D / 32], float sl2, int q0, int key,
+                                           int N, int causal, bool need_mask, int l32, int hh) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        float pv[16], dsv[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 L = *(const f32x4*)(lse2 + 32 * qb + 8 * g + 4 * hh);
+            const f32x4 Dd = *(const f32x4*)(dvec + 32 * qb + 8 * g + 4 * hh);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * g + i;
+                float pr = fast_exp2(__builtin_fmaf(s[qb][r], sl2, -L[i]));
+                if (need_mask) {
+                    const int qq = q0 + 32 * qb + 8 * g + 4 * hh + i;
+                    pr = (qq < N && (!causal || key <= qq)) ? pr : 0.f;
+                }
+                pv[r] = pr;
+                dsv[r] = pr * (dp[qb][r] - Dd[i]);
+            }
+        }
+        u32x4 pf[2], dsf[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pf[h2][j] = pack_bf16(pv[8 * h2 + 2 * j], pv[8 * h2 + 2 * j + 1]);
+                dsf[h2][j] = pack_bf16(dsv[8 * h2 + 2 * j], dsv[8 * h2 + 2 * j + 1]);
+            }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                dvt[db] = mfma32x32x16(permt_frag<D>(gtr, 32 * db + l32, 32 * qb + 16 * h2, hh), pf[h2], dvt[db]);
+                dkt[db] = mfma32x32x16(permt_frag<D>(qtr, 32 * db + l32, 32 * qb + 16 * h2, hh), dsf[h2], dkt[db]);
+            }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(DkdvCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
     using C = DkdvCfg<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (C::NSTAGE + C::TSTAGE)];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -118,103 +182,55 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     const int nitems = G * per_head;
     const float sl2 = p.scale_log2;
 
-    TileRegs<D> qr, gr;
+    // Per item (query head hq, 64-row tile at q0): natural Q and dO arrive by direct
+    // loads (one iteration ahead); the transposed, permuted copies are made from
+    // them in LDS, so each tile is read from L2 once.  Iteration it:
+    //   A. wait for this wave's loads of item it, barrier (item it's natural tiles
+    //      visible; everyone is done with iteration it-1);
+    //   B. direct loads of item it+1 into the other natural buffer, LSE/D of it+1;
+    //   C. transpose item it (threads of the first 4 waves, two 4x8 items each);
+    //   D. S and dP of item it on the matrix cores; barrier (transposes visible);
+    //   E. P, dS, dV and dK of item it.
+    constexpr int NS = C::NSTAGE;                 // natural Q, dO
+    constexpr int TS = C::TSTAGE;                 // transposed Q, dO, LSE*log2e, D
+    uint16_t* nat = smem;                         // item it at nat + (it&1)*NS
+    uint16_t* trs = smem + 2 * NS;                // item it at trs + (it&1)*TS
     float vec_reg = 0.f;
-    auto load_item = [&](int item) {
-        const int hq = hkv * G + item / per_head;
-        const int q0 = (qt_start + item % per_head) * C::BQ;
+    auto issue_item = [&](int it) {
+        const int hq = hkv * G + it / per_head;
+        const int q0 = (qt_start + it % per_head) * C::BQ;
         const size_t qoff = ((size_t)(b * p.Hq + hq) * N + q0) * D;
-        tile_load<D>(qr, (const uint16_t*)p.q + qoff, N - q0, tid);
-        tile_load<D>(gr, (const uint16_t*)p.dO + qoff, N - q0, tid);
+        uint16_t* st = nat + (it & 1) * NS;
+        swz_tile_issue<D, 2, C::WAVES>((const uint16_t*)p.q + qoff, N - q0, st, wave, lane);
+        swz_tile_issue<D, 2, C::WAVES>((const uint16_t*)p.dO + qoff, N - q0, st + C::NAT, wave, lane);
         const size_t roff = (size_t)(b * p.Hq + hq) * N + q0;
         if (tid < 64) vec_reg = q0 + tid < N ? p.lse[roff + tid] * kLog2e : 0.f;
         else if (tid < 128) vec_reg = q0 + tid - 64 < N ? p.dsum[roff + tid - 64] : 0.f;
     };
-    auto store_item = [&](uint16_t* st) {
-        tile_store_natural<D>(qr, st + C::QN, tid);
-        tile_store_transposed<D>(qr, st + C::QT, tid);
-        tile_store_natural<D>(gr, st + C::GN, tid);
-        tile_store_transposed<D>(gr, st + C::GT, tid);
-        if (tid < 128) ((float*)(st + C::VEC))[tid] = vec_reg;
-    };
 
-    if (nitems > 0) {
-        load_item(0);
-        store_item(smem);
-    }
-    __syncthreads();
-
+    if (nitems > 0) issue_item(0);
     for (int it = 0; it < nitems; ++it) {
-        const bool more = it + 1 < nitems;
-        if (more) load_item(it + 1);
-        const uint16_t* st = smem + (it & 1) * C::STAGE;
         const int q0 = (qt_start + it % per_head) * C::BQ;
-
-        if (kw0 < N && (!p.causal || q0 + C::BQ - 1 >= kw0)) {
-            // ---- S = Q K^T and dP = dO V^T with queries on the C rows
-            f32x16 s[2], dp[2];
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                s[qb] = zero16();
-                dp[qb] = zero16();
-            }
-#pragma unroll
-            for (int c = 0; c < C::DC; ++c)
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    s[qb] = mfma32x32x16(frag_natural<D>(st + C::QN, 32 * qb + l32, c, hh), kf[c], s[qb]);
-                    dp[qb] = mfma32x32x16(frag_natural<D>(st + C::GN, 32 * qb + l32, c, hh), vf[c], dp[qb]);
-                }
-
-            // ---- P = 2^(S*sl2 - LSE2), dS = P (dP - D)
-            const bool need_mask = (p.causal && q0 < kw0 + 31) || (q0 + C::BQ > N);
-            const float* lse2 = (const float*)(st + C::VEC);
-            const float* dvec = lse2 + 64;
-            u32x4 pf[2][2], dsf[2][2];
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                float pv[16], dsv[16];
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 L = *(const f32x4*)(lse2 + 32 * qb + 8 * g + 4 * hh);
-                    const f32x4 Dd = *(const f32x4*)(dvec + 32 * qb + 8 * g + 4 * hh);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = 4 * g + i;
-                        float pr = fast_exp2(__builtin_fmaf(s[qb][r], sl2, -L[i]));
-                        if (need_mask) {
-                            const int q = q0 + 32 * qb + 8 * g + 4 * hh + i;
-                            pr = (q < N && (!p.causal || key <= q)) ? pr : 0.f;
-                        }
-                        pv[r] = pr;
-                        dsv[r] = pr * (dp[qb][r] - Dd[i]);
-                    }
-                }
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        pf[qb][h2][j] = pack_bf16(pv[8 * h2 + 2 * j], pv[8 * h2 + 2 * j + 1]);
-                        dsf[qb][h2][j] = pack_bf16(dsv[8 * h2 + 2 * j], dsv[8 * h2 + 2 * j + 1]);
-                    }
-            }
-
-            // ---- dV^T += dO^T P,  dK^T += Q^T dS   (contractions over the query rows)
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                    for (int db = 0; db < C::DB; ++db) {
-                        const u32x4 ga = frag_transposed<D>(st + C::GT, 32 * db + l32, 32 * qb + 16 * h2, hh);
-                        dvt[db] = mfma32x32x16(ga, pf[qb][h2], dvt[db]);
-                        const u32x4 qa = frag_transposed<D>(st + C::QT, 32 * db + l32, 32 * qb + 16 * h2, hh);
-                        dkt[db] = mfma32x32x16(qa, dsf[qb][h2], dkt[db]);
-                    }
+        const uint16_t* nb = nat + (it & 1) * NS;
+        uint16_t* tb = trs + (it & 1) * TS;
+        float* vec = (float*)(tb + 2 * C::TR);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();                                           // A
+        if (tid < 128) vec[tid] = vec_reg;
+        if (it + 1 < nitems) issue_item(it + 1);                   // B
+        if (tid < PermT<D>::ITEMS) {                               // C
+            permt_from_lds<D, 2>(nb, tb, N - q0, tid);
+            permt_from_lds<D, 2>(nb + C::NAT, tb + C::TR, N - q0, tid);
         }
-
-        if (more) store_item(smem + ((it + 1) & 1) * C::STAGE);
+        const bool act = kw0 < N && (!p.causal || q0 + C::BQ - 1 >= kw0);
+        f32x16 sc[2], dp[2];
+        if (act) dkdv_scores<D>(nb, nb + C::NAT, kf, vf, sc, dp, l32, hh);   // D
         __syncthreads();
+        if (act) {                                                 // E
+            const bool need_mask = (p.causal && q0 < kw0 + 31) || (q0 + C::BQ > N);
+            dkdv_grads<D>(sc, dp, tb, tb + C::TR, vec, vec + 64, dkt, dvt, sl2, q0, key, N, p.causal, need_mask,
+                          l32, hh);
+        }
     }
 
     if (key < N) {
@@ -237,25 +253,24 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------------
-template <int D, int QB>
+template <int D>
 struct DqCfg {
-    static constexpr int BR = kWaves * 32 * QB;
+    static constexpr int WAVES = 8;
+    static constexpr int THREADS = WAVES * kWave;
+    static constexpr int BR = WAVES * 32;
     static constexpr int BC = 64;
     static constexpr int DC = D / 16;
     static constexpr int DB = D / 32;
-    using T = Tile64<D>;
-    static constexpr int KN = 0;
-    static constexpr int KT = KN + T::N_ELEMS;
-    static constexpr int VN = KT + T::T_ELEMS;
-    static constexpr int STAGE = VN + T::N_ELEMS;
+    static constexpr int NAT = SwzTile<D, 0>::ELEMS;
+    static constexpr int TR = PermT<D>::ELEMS;
+    static constexpr int STAGE = 2 * NAT + TR;   // K natural, V natural, K transposed
 };
 
-constexpr int kDqQB = 1;
-
-template <int D, int QB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D>
+__global__ __launch_bounds__(DqCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(BwdParams p) {
-    using C = DqCfg<D, QB>;
+    using C = DqCfg<D>;
+    using NT = SwzTile<D, 0>;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
 
     const int tid = threadIdx.x;
@@ -277,131 +292,106 @@ void fa_bwd_dq_kernel(BwdParams p) {
     const uint16_t* Vh = (const uint16_t*)p.v + kvoff;
 
     const int q0 = qt * C::BR;
-    const int qw0 = q0 + wave * 32 * QB;
+    const int qw0 = q0 + wave * 32;
+    const int q = qw0 + l32;
     const int q_last = min(q0 + C::BR, N) - 1;
     const int ntiles = p.causal ? q_last / C::BC + 1 : (N + C::BC - 1) / C::BC;
-    const int wq_last = min(qw0 + 32 * QB, N) - 1;
+    const int wq_last = min(qw0 + 32, N) - 1;
     const int wave_tiles = wq_last < qw0 ? 0 : (p.causal ? wq_last / C::BC + 1 : ntiles);
 
-    u32x4 qf[QB][C::DC], gf[QB][C::DC];
-    float lse2[QB], dd[QB];
-    f32x16 dqt[C::DB][QB];
+    // Q and dO as B operands of S^T = K Q^T and dP^T = V dO^T (lane: query)
+    u32x4 qf[C::DC], gf[C::DC];
+    const bool ok = q < N;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int q = qw0 + 32 * qb + l32;
-        const bool ok = q < N;
-#pragma unroll
-        for (int c = 0; c < C::DC; ++c) {
-            qf[qb][c] = ok ? ld_global16((const uint16_t*)p.q + qoff + (size_t)q * D + 16 * c + 8 * hh) : zero_u4();
-            gf[qb][c] = ok ? ld_global16((const uint16_t*)p.dO + qoff + (size_t)q * D + 16 * c + 8 * hh) : zero_u4();
-        }
-        lse2[qb] = ok ? p.lse[(size_t)head * N + q] * kLog2e : 0.f;
-        dd[qb] = ok ? p.dsum[(size_t)head * N + q] : 0.f;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) dqt[db][qb] = zero16();
+    for (int c = 0; c < C::DC; ++c) {
+        qf[c] = ok ? ld_global16((const uint16_t*)p.q + qoff + (size_t)q * D + 16 * c + 8 * hh) : zero_u4();
+        gf[c] = ok ? ld_global16((const uint16_t*)p.dO + qoff + (size_t)q * D + 16 * c + 8 * hh) : zero_u4();
     }
+    const float lse2 = ok ? p.lse[(size_t)head * N + q] * kLog2e : 0.f;
+    const float dd = ok ? p.dsum[(size_t)head * N + q] : 0.f;
+    f32x16 dqt[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) dqt[db] = zero16();
     const float sl2 = p.scale_log2;
 
-    TileRegs<D> kr, vr;
-    tile_load<D>(kr, Kh, N, tid);
-    tile_load<D>(vr, Vh, N, tid);
-    tile_store_natural<D>(kr, smem + C::KN, tid);
-    tile_store_transposed<D>(kr, smem + C::KT, tid);
-    tile_store_natural<D>(vr, smem + C::VN, tid);
+    const bool stager = tid < PermT<D>::ITEMS;
+    u32x4 kr[4];
+    auto load_tile = [&](int t, uint16_t* st) {
+        const int k0 = t * C::BC;
+        swz_tile_issue<D, 0, C::WAVES>(Kh + (size_t)k0 * D, N - k0, st, wave, lane);
+        swz_tile_issue<D, 0, C::WAVES>(Vh + (size_t)k0 * D, N - k0, st + C::NAT, wave, lane);
+        if (stager) permt_load<D>(kr, Kh + (size_t)k0 * D, N - k0, tid);
+    };
+
+    load_tile(0, smem);
+    if (stager) permt_store<D>(kr, smem + 2 * C::NAT, tid);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int t = 0; t < ntiles; ++t) {
         const int k0 = t * C::BC;
         const bool more = t + 1 < ntiles;
-        if (more) {
-            tile_load<D>(kr, Kh + (size_t)(k0 + C::BC) * D, N - (k0 + C::BC), tid);
-            tile_load<D>(vr, Vh + (size_t)(k0 + C::BC) * D, N - (k0 + C::BC), tid);
-        }
+        uint16_t* nb = smem + ((t + 1) & 1) * C::STAGE;
+        if (more) load_tile(t + 1, nb);
         const uint16_t* st = smem + (t & 1) * C::STAGE;
 
         if (t < wave_tiles) {
-            f32x16 s[2][QB], dp[2][QB];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    s[kb][qb] = zero16();
-                    dp[kb][qb] = zero16();
-                }
+            f32x16 s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
 #pragma unroll
             for (int c = 0; c < C::DC; ++c)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const u32x4 ka = frag_natural<D>(st + C::KN, 32 * kb + l32, c, hh);
-                    const u32x4 va = frag_natural<D>(st + C::VN, 32 * kb + l32, c, hh);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) {
-                        s[kb][qb] = mfma32x32x16(ka, qf[qb][c], s[kb][qb]);
-                        dp[kb][qb] = mfma32x32x16(va, gf[qb][c], dp[kb][qb]);
-                    }
+                    s[kb] = mfma32x32x16(lds16(st + NT::at(32 * kb + l32, 2 * c + hh)), qf[c], s[kb]);
+                    dp[kb] = mfma32x32x16(lds16(st + C::NAT + NT::at(32 * kb + l32, 2 * c + hh)), gf[c], dp[kb]);
                 }
-
-            const bool need_mask = (p.causal && k0 + C::BC - 1 > qw0) || (k0 + C::BC > N);
-            u32x4 dsf[QB][2][2];
+            if ((p.causal && k0 + C::BC - 1 > qw0) || (k0 + C::BC > N)) {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const int q = qw0 + 32 * qb + l32;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    float dsv[16];
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        float pr = fast_exp2(__builtin_fmaf(s[kb][qb][r], sl2, -lse2[qb]));
-                        if (need_mask) {
-                            const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                            pr = (kk < N && (!p.causal || kk <= q)) ? pr : 0.f;
-                        }
-                        dsv[r] = pr * (dp[kb][qb][r] - dd[qb]);
+                        const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+                        const bool vis = kk < N && (!p.causal || kk <= q);
+                        s[kb][r] = vis ? s[kb][r] : kNegInf;   // -inf * sl2 - lse2 -> p = 0
                     }
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            dsf[qb][kb][h2][j] = pack_bf16(dsv[8 * h2 + 2 * j], dsv[8 * h2 + 2 * j + 1]);
-                }
             }
-
+            u32x4 dsf[2][2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 8 * h2 + 2 * j;
+                        const float pa = fast_exp2(__builtin_fmaf(s[kb][r], sl2, -lse2));
+                        const float pb = fast_exp2(__builtin_fmaf(s[kb][r + 1], sl2, -lse2));
+                        dsf[kb][h2][j] = pack_bf16(pa * (dp[kb][r] - dd), pb * (dp[kb][r + 1] - dd));
+                    }
             // ---- dQ^T += K^T dS^T  (contraction over the keys)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-                    for (int db = 0; db < C::DB; ++db) {
-                        const u32x4 ka = frag_transposed<D>(st + C::KT, 32 * db + l32, 32 * kb + 16 * h2, hh);
-#pragma unroll
-                        for (int qb = 0; qb < QB; ++qb) dqt[db][qb] = mfma32x32x16(ka, dsf[qb][kb][h2], dqt[db][qb]);
-                    }
+                    for (int db = 0; db < C::DB; ++db)
+                        dqt[db] = mfma32x32x16(permt_frag<D>(st + 2 * C::NAT, 32 * db + l32, 32 * kb + 16 * h2, hh),
+                                               dsf[kb][h2], dqt[db]);
         }
 
-        if (more) {
-            uint16_t* nb = smem + ((t + 1) & 1) * C::STAGE;
-            tile_store_natural<D>(kr, nb + C::KN, tid);
-            tile_store_transposed<D>(kr, nb + C::KT, tid);
-            tile_store_natural<D>(vr, nb + C::VN, tid);
-        }
+        if (more && stager) permt_store<D>(kr, nb + 2 * C::NAT, tid);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
-    const float sc = p.scale;
+    if (ok) {
+        uint16_t* dQh = (uint16_t*)p.dq + qoff + (size_t)q * D;
+        const float sc = p.scale;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int q = qw0 + 32 * qb + l32;
-        if (q < N) {
-            uint16_t* dQh = (uint16_t*)p.dq + qoff + (size_t)q * D;
+        for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    *(u32x2*)(dQh + 32 * db + 8 * g + 4 * hh) =
-                        u32x2{pack_bf16(dqt[db][qb][4 * g] * sc, dqt[db][qb][4 * g + 1] * sc),
-                              pack_bf16(dqt[db][qb][4 * g + 2] * sc, dqt[db][qb][4 * g + 3] * sc)};
-        }
+            for (int g = 0; g < 4; ++g)
+                *(u32x2*)(dQh + 32 * db + 8 * g + 4 * hh) =
+                    u32x2{pack_bf16(dqt[db][4 * g] * sc, dqt[db][4 * g + 1] * sc),
+                          pack_bf16(dqt[db][4 * g + 2] * sc, dqt[db][4 * g + 3] * sc)};
     }
 }
 
@@ -411,7 +401,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
 long long bwd_grid_max(int B, int Hq, int Hkv, int N, int d) {
     const long long pre = ((long long)B * Hq * N * (d / 8) + kThreads - 1) / kThreads;
     const long long dkdv = (long long)B * Hkv * ((N + 127) / 128);
-    const long long dq = (long long)B * Hq * ((N + kWaves * 32 * kDqQB - 1) / (kWaves * 32 * kDqQB));
+    const long long dq = (long long)B * Hq * ((N + 255) / 256);
     long long m = pre > dkdv ? pre : dkdv;
     return m > dq ? m : dq;
 }
@@ -428,15 +418,15 @@ static hipError_t launch_pre(const BwdParams& p, hipStream_t stream) {
 template <int D>
 static hipError_t launch_dkdv(const BwdParams& p, hipStream_t stream) {
     const unsigned blocks = (unsigned)((long long)p.B * p.Hkv * ((p.N + DkdvCfg<D>::BK - 1) / DkdvCfg<D>::BK));
-    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<D>, dim3(blocks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<D>, dim3(blocks), dim3(DkdvCfg<D>::THREADS), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_dq(const BwdParams& p, hipStream_t stream) {
-    constexpr int br = DqCfg<D, kDqQB>::BR;
+    constexpr int br = DqCfg<D>::BR;
     const unsigned blocks = (unsigned)((long long)p.B * p.Hq * ((p.N + br - 1) / br));
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, kDqQB>), dim3(blocks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(fa_bwd_dq_kernel<D>, dim3(blocks), dim3(DqCfg<D>::THREADS), 0, stream, p);
     return hipGetLastError();
 }
 

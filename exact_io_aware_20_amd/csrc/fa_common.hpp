@@ -187,11 +187,13 @@ struct SwzTile {
     static constexpr int CHUNKS = D / 8;          // 16-byte chunks per row
     static constexpr int ELEMS = 64 * D;          // bf16 elements per tile
     static constexpr int WAVE_LOADS = 64 * CHUNKS / kWave;   // wave-instructions per tile
-    // MODE 0 spreads 32 consecutive rows (fragment reads), MODE 1 spreads rows
-    // 4k + j for k = 0..15 (the transposing reads of permt_from_lds).
+    // MODE 0 spreads 32 consecutive rows (fragment reads); MODE 1 spreads rows
+    // 4k + j for k = 0..15 (transposing reads); MODE 2 spreads both (r ^ r/4 is a
+    // bijection on each 16 consecutive rows and on rows 4k + j).
     __device__ static __forceinline__ int swz(int r) {
         if (MODE == 0) return D == 128 ? (r & 15) : ((r >> 1) & 7);
-        return D == 128 ? ((r >> 2) & 15) : ((r >> 2) & 7);
+        if (MODE == 1) return D == 128 ? ((r >> 2) & 15) : ((r >> 2) & 7);
+        return D == 128 ? ((r ^ (r >> 2)) & 15) : ((r ^ (r >> 2)) & 7);
     }
     // element offset of (row, chunk)
     __device__ static __forceinline__ int at(int r, int j) { return r * D + ((j ^ swz(r)) << 3); }
@@ -211,15 +213,15 @@ __device__ __forceinline__ int opaque(int x) {
 // covers LDS chunk positions [64 i, 64 i + 64).  Rows at or past `nvalid` are
 // read from row nvalid-1 instead (always in bounds; callers mask those rows or
 // give them zero weight).
-template <int D, int MODE = 0>
+template <int D, int MODE, int NWAVES>
 __device__ __forceinline__ int swz_tile_issue(const uint16_t* src, int nvalid, uint16_t* lds_tile,
-                                              int wave, int nwaves, int lane) {
+                                              int wave, int lane) {
     using S = SwzTile<D, MODE>;
     lane = opaque(lane);
     int issued = 0;
 #pragma unroll
-    for (int k = 0; k < (S::WAVE_LOADS + 7) / 8; ++k) {
-        const int i = wave + k * nwaves;
+    for (int k = 0; k < (S::WAVE_LOADS + NWAVES - 1) / NWAVES; ++k) {
+        const int i = wave + k * NWAVES;
         if (i < S::WAVE_LOADS) {
             const int pos = i * 64 + lane;
             const int r = pos / S::CHUNKS;
@@ -250,15 +252,15 @@ struct PadTile {
     __device__ static __forceinline__ int at(int r, int j) { return r * STR + j * 8; }
 };
 
-template <int D>
+template <int D, int NWAVES>
 __device__ __forceinline__ int pad_tile_issue(const uint16_t* src, int nvalid, uint16_t* lds_tile, int wave,
-                                              int nwaves, int lane) {
+                                              int lane) {
     using P = PadTile<D>;
     lane = opaque(lane);
     int issued = 0;
 #pragma unroll
-    for (int k = 0; k < (P::WAVE_LOADS + 7) / 8; ++k) {
-        const int i = wave + k * nwaves;
+    for (int k = 0; k < (P::WAVE_LOADS + NWAVES - 1) / NWAVES; ++k) {
+        const int i = wave + k * NWAVES;
         if (i < P::WAVE_LOADS) {
             const int pos = i * 64 + lane;
             const int r = pos / P::SLOTS;
@@ -317,12 +319,12 @@ __device__ __forceinline__ void permt_store(const u32x4 (&r)[4], uint16_t* dst, 
     }
 }
 
-// Transpose one item (4 keys x 8 columns) from a MODE 1 swizzled natural tile in
+// Transpose one item (4 keys x 8 columns) from a MODE 1 or 2 swizzled natural tile in
 // LDS into the permuted transposed layout.  Rows >= nvalid are written as zero, so
 // stale or clamped rows contribute nothing to P.V.
-template <int D>
+template <int D, int MODE = 1>
 __device__ __forceinline__ void permt_from_lds(const uint16_t* src, uint16_t* dst, int nvalid, int item) {
-    using S = SwzTile<D, 1>;
+    using S = SwzTile<D, MODE>;
     item = opaque(item);
     const int kq = item % 16, c = item / 16;
     u32x4 r[4];

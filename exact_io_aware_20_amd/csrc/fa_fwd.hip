@@ -191,7 +191,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     const bool v_stager = tid < PermT<D>::ITEMS;
     u32x4 vr[4];
     auto issue_k = [&](int t, uint16_t* buf) {
-        swz_tile_issue<D, 0>(Kh + (size_t)t * C::BC * D, N - t * C::BC, buf, wave, C::WAVES, lane);
+        swz_tile_issue<D, 0, C::WAVES>(Kh + (size_t)t * C::BC * D, N - t * C::BC, buf, wave, lane);
     };
 
     // prologue: K(0), V(0) -> LDS; S(0); K(1) -> LDS
