@@ -58,92 +58,88 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_pre_kernel(const uint16_t* o,
 // ---------------------------------------------------------------------------------
 template <int D>
 struct DkdvCfg {
-    static constexpr int WAVES = 4;
+    static constexpr int WAVES = 8;          // 4 dK waves + 4 dV waves
     static constexpr int THREADS = WAVES * kWave;
-    static constexpr int BK = WAVES * 32;   // keys per workgroup
-    static constexpr int BQ = 64;           // query rows per streamed tile
+    static constexpr int BK = 4 * 32;        // keys per workgroup
+    static constexpr int BQ = 64;            // query rows per streamed tile
     static constexpr int DC = D / 16;
     static constexpr int DB = D / 32;
-    static constexpr int NAT = SwzTile<D, 0>::ELEMS;   // natural Q or dO tile
+    static constexpr int NAT = SwzTile<D, 2>::ELEMS;   // natural Q or dO tile
     static constexpr int TR = PermT<D>::ELEMS;         // transposed Q or dO tile
-    static constexpr int NSTAGE = 2 * NAT;                 // natural Q, dO
-    static constexpr int TSTAGE = 2 * TR + 2 * 64 * 2;     // transposed Q, dO; LSE*log2e, D (fp32)
+    static constexpr int NSTAGE = 2 * NAT;             // natural Q, dO (double-buffered)
+    static constexpr int TSTAGE = 2 * TR + 2 * 64 * 2; // transposed Q, dO; LSE*log2e, D (fp32)
 };
 
-// Per streamed tile and wave (32 keys x 64 queries in two 32-query halves qb):
-// S = Q K^T and dP = dO V^T with the queries on the C rows.
+// C[q][key] = sum_d A[q][d] B[key][d] for query half qb (32 rows) of a natural
+// tile and the wave's 32 keys (B fragments in registers): queries on the C rows.
 template <int D>
-__device__ __forceinline__ void dkdv_scores(const uint16_t* qn, const uint16_t* gn, const u32x4 (&kf)[D / 16],
-                                            const u32x4 (&vf)[D / 16], f32x16 (&s)[2], f32x16 (&dp)[2], int l32,
-                                            int hh) {
+__device__ __forceinline__ f32x16 qk_half(const uint16_t* nat, const u32x4 (&bf)[D / 16], int qb, int l32, int hh) {
     using NT = SwzTile<D, 2>;
+    f32x16 c = zero16();
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = zero16();
-        dp[qb] = zero16();
+    for (int k = 0; k < D / 16; ++k) c = mfma32x32x16(lds16(nat + NT::at(32 * qb + l32, 2 * k + hh)), bf[k], c);
+    return c;
+}
+
+// Set S to -inf where key > query (causal) or the query row is >= N, so that
+// 2^(S*sl2 - LSE2) is exactly 0 there.  Queries of register r: qrow0 + 8(r/4) + r%4.
+__device__ __forceinline__ void mask_half(f32x16& s, int qrow0, int key, int N, int causal) {
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-            s[qb] = mfma32x32x16(lds16(qn + NT::at(32 * qb + l32, 2 * c + hh)), kf[c], s[qb]);
-            dp[qb] = mfma32x32x16(lds16(gn + NT::at(32 * qb + l32, 2 * c + hh)), vf[c], dp[qb]);
-        }
+    for (int r = 0; r < 16; ++r) {
+        const int qq = qrow0 + 8 * (r >> 2) + (r & 3);
+        s[r] = (qq < N && (!causal || key <= qq)) ? s[r] : kNegInf;
     }
 }
 
-// Then half by half: P = 2^(S*sl2 - LSE2), dS = P (dP - D) on the vector ALU and
-// dV^T += dO^T P, dK^T += Q^T dS on the matrix cores, so that one half's products
-// overlap the other half's vector work.  Queries of register r: 32*qb + 8*(r/4) +
-// 4*hh + r%4.
-template <int D>
-__device__ __forceinline__ void dkdv_grads(const f32x16 (&s)[2], const f32x16 (&dp)[2], const uint16_t* qtr,
-                                           const uint16_t* gtr, const float* lse2, const float* dvec,
-                                           f32x16 (&dkt)[D / 32], f32x16 (&dvt)[D / 32], float sl2, int q0, int key,
-                                           int N, int causal, bool need_mask, int l32, int hh) {
+// One query half: P = 2^(S*sl2 - LSE2); dK waves form dS = P (dP - D) and
+// accumulate dK^T += Q^T dS, dV waves accumulate dV^T += dO^T P.  Register 4g+i
+// of a C tile is k-slot 4(g%2)+i of fragment g/2 (query 8g + 4hh + i of the half).
+template <int D, bool DK>
+__device__ __forceinline__ void grads_half(const f32x16& s, const f32x16& dp, const uint16_t* tr, const float* lse2,
+                                           const float* dvec, f32x16 (&acc)[D / 32], float sl2, int qb, int l32,
+                                           int hh) {
+    u32x4 bf[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        float pv[16], dsv[16];
+    for (int g = 0; g < 4; ++g) {
+        const f32x4 L = *(const f32x4*)(lse2 + 32 * qb + 8 * g + 4 * hh);
+        float pv[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const f32x4 L = *(const f32x4*)(lse2 + 32 * qb + 8 * g + 4 * hh);
+        for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(__builtin_fmaf(s[4 * g + i], sl2, -L[i]));
+        if (DK) {
             const f32x4 Dd = *(const f32x4*)(dvec + 32 * qb + 8 * g + 4 * hh);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * g + i;
-                float pr = fast_exp2(__builtin_fmaf(s[qb][r], sl2, -L[i]));
-                if (need_mask) {
-                    const int qq = q0 + 32 * qb + 8 * g + 4 * hh + i;
-                    pr = (qq < N && (!causal || key <= qq)) ? pr : 0.f;
-                }
-                pv[r] = pr;
-                dsv[r] = pr * (dp[qb][r] - Dd[i]);
-            }
+            for (int i = 0; i < 4; ++i) pv[i] *= dp[4 * g + i] - Dd[i];
         }
-        u32x4 pf[2], dsf[2];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                pf[h2][j] = pack_bf16(pv[8 * h2 + 2 * j], pv[8 * h2 + 2 * j + 1]);
-                dsf[h2][j] = pack_bf16(dsv[8 * h2 + 2 * j], dsv[8 * h2 + 2 * j + 1]);
-            }
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                dvt[db] = mfma32x32x16(permt_frag<D>(gtr, 32 * db + l32, 32 * qb + 16 * h2, hh), pf[h2], dvt[db]);
-                dkt[db] = mfma32x32x16(permt_frag<D>(qtr, 32 * db + l32, 32 * qb + 16 * h2, hh), dsf[h2], dkt[db]);
-            }
+        bf[g >> 1][2 * (g & 1)] = pack_bf16(pv[0], pv[1]);
+        bf[g >> 1][2 * (g & 1) + 1] = pack_bf16(pv[2], pv[3]);
     }
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+            acc[db] = mfma32x32x16(permt_frag<D>(tr, 32 * db + l32, 32 * qb + 16 * h2, hh), bf[h2], acc[db]);
 }
 
-template <int D>
-__global__ __launch_bounds__(DkdvCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void fa_bwd_dkdv_kernel(BwdParams p) {
+// dK/dV kernel.  A workgroup owns 128 keys of one KV head; waves 0-3 accumulate
+// dK and waves 4-7 dV for keys 32(w%4) .. +31, so each wave holds one accumulator
+// set and two waves fit per SIMD (the dK and dV waves of a key block share one).
+// Both recompute S; the dK wave also forms dP.  64-row query tiles of every query
+// head of the group stream through LDS.  Iteration it:
+//   A. wait for this wave's loads of item it, barrier;
+//   B. direct loads of item it+1 (natural Q, dO) into the other buffer, LSE/D;
+//   C. transposed, permuted Q and dO of item it built in LDS (one 4x8 item per thread);
+//   D. S (and dP) of the first query half; barrier;
+//   E. gradients of the first half while S (and dP) of the second half run on the
+//      matrix cores, then the gradients of the second half.
+template <int D, bool DK>
+__device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, int tid, int wave, int lane) {
     using C = DkdvCfg<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (C::NSTAGE + C::TSTAGE)];
+    constexpr int NS = C::NSTAGE;
+    uint16_t* nat = smem;              // item it: natural Q at nat + (it&1)*NS, dO at + NAT
+    uint16_t* trs = smem + 2 * NS;     // transposed Q, dO, then LSE*log2e and D of the current item
+    float* vec = (float*)(trs + 2 * C::TR);
+    const uint16_t* my_tr = trs + (DK ? 0 : C::TR);
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;
     const int hh = lane >> 5;
     const int N = p.N;
@@ -155,26 +151,20 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     const int b = head_kv / p.Hkv;
     const int hkv = head_kv % p.Hkv;
     const int k0 = kt * C::BK;
-    const int kw0 = k0 + 32 * wave;
+    const int kw0 = k0 + 32 * (wave & 3);
     const int key = kw0 + l32;
 
     const size_t kvoff = (size_t)head_kv * N * D;
-    const uint16_t* Kh = (const uint16_t*)p.k + kvoff;
-    const uint16_t* Vh = (const uint16_t*)p.v + kvoff;
-
-    // K and V as B operands of S = Q K^T and dP = dO V^T (lane: key, slots: 8 d)
-    u32x4 kf[C::DC], vf[C::DC];
+    // K (both roles) and V (dK waves) as B operands (lane: key, slots: 8 d)
+    u32x4 kf[C::DC], vf[DK ? C::DC : 1];
 #pragma unroll
     for (int c = 0; c < C::DC; ++c) {
-        kf[c] = key < N ? ld_global16(Kh + (size_t)key * D + 16 * c + 8 * hh) : zero_u4();
-        vf[c] = key < N ? ld_global16(Vh + (size_t)key * D + 16 * c + 8 * hh) : zero_u4();
+        kf[c] = key < N ? ld_global16((const uint16_t*)p.k + kvoff + (size_t)key * D + 16 * c + 8 * hh) : zero_u4();
+        if constexpr (DK) vf[c] = key < N ? ld_global16((const uint16_t*)p.v + kvoff + (size_t)key * D + 16 * c + 8 * hh) : zero_u4();
     }
-    f32x16 dkt[C::DB], dvt[C::DB];
+    f32x16 acc[C::DB];
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-        dkt[db] = zero16();
-        dvt[db] = zero16();
-    }
+    for (int db = 0; db < C::DB; ++db) acc[db] = zero16();
 
     const int nqt = (N + C::BQ - 1) / C::BQ;
     const int qt_start = p.causal ? k0 / C::BQ : 0;
@@ -182,19 +172,6 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     const int nitems = G * per_head;
     const float sl2 = p.scale_log2;
 
-    // Per item (query head hq, 64-row tile at q0): natural Q and dO arrive by direct
-    // loads (one iteration ahead); the transposed, permuted copies are made from
-    // them in LDS, so each tile is read from L2 once.  Iteration it:
-    //   A. wait for this wave's loads of item it, barrier (item it's natural tiles
-    //      visible; everyone is done with iteration it-1);
-    //   B. direct loads of item it+1 into the other natural buffer, LSE/D of it+1;
-    //   C. transpose item it (threads of the first 4 waves, two 4x8 items each);
-    //   D. S and dP of item it on the matrix cores; barrier (transposes visible);
-    //   E. P, dS, dV and dK of item it.
-    constexpr int NS = C::NSTAGE;                 // natural Q, dO
-    constexpr int TS = C::TSTAGE;                 // transposed Q, dO, LSE*log2e, D
-    uint16_t* nat = smem;                         // item it at nat + (it&1)*NS
-    uint16_t* trs = smem + 2 * NS;                // item it at trs + (it&1)*TS
     float vec_reg = 0.f;
     auto issue_item = [&](int it) {
         const int hq = hkv * G + it / per_head;
@@ -212,42 +189,55 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     for (int it = 0; it < nitems; ++it) {
         const int q0 = (qt_start + it % per_head) * C::BQ;
         const uint16_t* nb = nat + (it & 1) * NS;
-        uint16_t* tb = trs + (it & 1) * TS;
-        float* vec = (float*)(tb + 2 * C::TR);
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();                                           // A
+        __syncthreads();                                            // A
         if (tid < 128) vec[tid] = vec_reg;
-        if (it + 1 < nitems) issue_item(it + 1);                   // B
-        if (tid < PermT<D>::ITEMS) {                               // C
-            permt_from_lds<D, 2>(nb, tb, N - q0, tid);
-            permt_from_lds<D, 2>(nb + C::NAT, tb + C::TR, N - q0, tid);
+        if (it + 1 < nitems) issue_item(it + 1);                    // B
+        {                                                           // C
+            const int which = tid / PermT<D>::ITEMS;                // 0: Q, 1: dO
+            if (which < 2) permt_from_lds<D, 2>(nb + which * C::NAT, trs + which * C::TR, N - q0, tid % PermT<D>::ITEMS);
         }
         const bool act = kw0 < N && (!p.causal || q0 + C::BQ - 1 >= kw0);
-        f32x16 sc[2], dp[2];
-        if (act) dkdv_scores<D>(nb, nb + C::NAT, kf, vf, sc, dp, l32, hh);   // D
+        const bool mask = (p.causal && q0 < kw0 + 31) || (q0 + C::BQ > N);
+        f32x16 s0, d0 = zero16();
+        if (act) {                                                  // D
+            s0 = qk_half<D>(nb, kf, 0, l32, hh);
+            if constexpr (DK) d0 = qk_half<D>(nb + C::NAT, vf, 0, l32, hh);
+        }
         __syncthreads();
-        if (act) {                                                 // E
-            const bool need_mask = (p.causal && q0 < kw0 + 31) || (q0 + C::BQ > N);
-            dkdv_grads<D>(sc, dp, tb, tb + C::TR, vec, vec + 64, dkt, dvt, sl2, q0, key, N, p.causal, need_mask,
-                          l32, hh);
+        if (act) {                                                  // E
+            if (mask) mask_half(s0, q0 + 4 * hh, key, N, p.causal);
+            grads_half<D, DK>(s0, d0, my_tr, vec, vec + 64, acc, sl2, 0, l32, hh);
+            f32x16 s1 = qk_half<D>(nb, kf, 1, l32, hh), d1 = zero16();
+            if constexpr (DK) d1 = qk_half<D>(nb + C::NAT, vf, 1, l32, hh);
+            if (mask) mask_half(s1, q0 + 32 + 4 * hh, key, N, p.causal);
+            grads_half<D, DK>(s1, d1, my_tr, vec, vec + 64, acc, sl2, 1, l32, hh);
         }
     }
 
     if (key < N) {
-        uint16_t* dKh = (uint16_t*)p.dk + kvoff + (size_t)key * D;
-        uint16_t* dVh = (uint16_t*)p.dv + kvoff + (size_t)key * D;
-        const float sc = p.scale;
+        uint16_t* dst = (uint16_t*)(DK ? p.dk : p.dv) + kvoff + (size_t)key * D;
+        const float sc = DK ? p.scale : 1.f;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = 32 * db + 8 * g + 4 * hh;
-                *(u32x2*)(dKh + d0) = u32x2{pack_bf16(dkt[db][4 * g] * sc, dkt[db][4 * g + 1] * sc),
-                                            pack_bf16(dkt[db][4 * g + 2] * sc, dkt[db][4 * g + 3] * sc)};
-                *(u32x2*)(dVh + d0) = u32x2{pack_bf16(dvt[db][4 * g], dvt[db][4 * g + 1]),
-                                            pack_bf16(dvt[db][4 * g + 2], dvt[db][4 * g + 3])};
-            }
+            for (int g = 0; g < 4; ++g)
+                *(u32x2*)(dst + 32 * db + 8 * g + 4 * hh) =
+                    u32x2{pack_bf16(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc),
+                          pack_bf16(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc)};
     }
+}
+
+template <int D>
+__global__ __launch_bounds__(DkdvCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dkdv_kernel(BwdParams p) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * DkdvCfg<D>::NSTAGE + DkdvCfg<D>::TSTAGE];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (wave < 4)
+        dkdv_role<D, true>(p, smem, tid, wave, tid & 63);
+    else
+        dkdv_role<D, false>(p, smem, tid, wave, tid & 63);
 }
 
 // ---------------------------------------------------------------------------------
