@@ -64,7 +64,7 @@ struct DkdvCfg {
     static constexpr int BQ = 64;            // query rows per streamed tile
     static constexpr int DC = D / 16;
     static constexpr int DB = D / 32;
-    static constexpr int NAT = SwzTile<D, 2>::ELEMS;   // natural Q or dO tile
+    static constexpr int NAT = SwzTile<D, 1>::ELEMS;   // natural Q or dO tile
     static constexpr int TR = PermT<D>::ELEMS;         // transposed Q or dO tile
     static constexpr int NSTAGE = 2 * NAT;             // natural Q, dO (double-buffered)
     static constexpr int TSTAGE = 2 * TR + 2 * 64 * 2; // transposed Q, dO; LSE*log2e, D (fp32)
@@ -74,7 +74,7 @@ struct DkdvCfg {
 // tile and the wave's 32 keys (B fragments in registers): queries on the C rows.
 template <int D>
 __device__ __forceinline__ f32x16 qk_half(const uint16_t* nat, const u32x4 (&bf)[D / 16], int qb, int l32, int hh) {
-    using NT = SwzTile<D, 2>;
+    using NT = SwzTile<D, 1>;
     f32x16 c = zero16();
 #pragma unroll
     for (int k = 0; k < D / 16; ++k) c = mfma32x32x16(lds16(nat + NT::at(32 * qb + l32, 2 * k + hh)), bf[k], c);
@@ -178,8 +178,8 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, in
         const int q0 = (qt_start + it % per_head) * C::BQ;
         const size_t qoff = ((size_t)(b * p.Hq + hq) * N + q0) * D;
         uint16_t* st = nat + (it & 1) * NS;
-        swz_tile_issue<D, 2, C::WAVES>((const uint16_t*)p.q + qoff, N - q0, st, wave, lane);
-        swz_tile_issue<D, 2, C::WAVES>((const uint16_t*)p.dO + qoff, N - q0, st + C::NAT, wave, lane);
+        swz_tile_issue<D, 1, C::WAVES>((const uint16_t*)p.q + qoff, N - q0, st, wave, lane);
+        swz_tile_issue<D, 1, C::WAVES>((const uint16_t*)p.dO + qoff, N - q0, st + C::NAT, wave, lane);
         const size_t roff = (size_t)(b * p.Hq + hq) * N + q0;
         if (tid < 64) vec_reg = q0 + tid < N ? p.lse[roff + tid] * kLog2e : 0.f;
         else if (tid < 128) vec_reg = q0 + tid - 64 < N ? p.dsum[roff + tid - 64] : 0.f;
@@ -195,7 +195,7 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, in
         if (it + 1 < nitems) issue_item(it + 1);                    // B
         {                                                           // C
             const int which = tid / PermT<D>::ITEMS;                // 0: Q, 1: dO
-            if (which < 2) permt_from_lds<D, 2>(nb + which * C::NAT, trs + which * C::TR, N - q0, tid % PermT<D>::ITEMS);
+            if (which < 2) permt_from_lds<D, 1>(nb + which * C::NAT, trs + which * C::TR, N - q0, tid % PermT<D>::ITEMS);
         }
         const bool act = kw0 < N && (!p.causal || q0 + C::BQ - 1 >= kw0);
         const bool mask = (p.causal && q0 < kw0 + 31) || (q0 + C::BQ > N);
