@@ -47,11 +47,11 @@ def load_library() -> ctypes.CDLL:
     lib.fa_forward_f32.restype = i
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
     lib.fa_backward.restype = i
-    lib.fa_backward_preprocess.argtypes = [vp, vp, vp, sz, i, i, i, i, vp]
+    lib.fa_backward_preprocess.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, vp]
     lib.fa_backward_preprocess.restype = i
-    lib.fa_backward_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_backward_dkdv.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, i, i, f, vp]
     lib.fa_backward_dkdv.restype = i
-    lib.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, i, f, vp]
     lib.fa_backward_dq.restype = i
     lib.fa_backward_workspace_bytes.argtypes = [i, i, i]
     lib.fa_backward_workspace_bytes.restype = sz
@@ -162,14 +162,14 @@ def backward_steps(q, k, v, o, do, lse, causal: bool, scale: float, dq, dk, dv, 
     wsb = workspace.numel() * workspace.element_size()
     for step in steps:
         if step == "pre":
-            code = lib.fa_backward_preprocess(o.data_ptr(), do.data_ptr(), workspace.data_ptr(), wsb,
-                                              B, Hq, N, d, st)
+            code = lib.fa_backward_preprocess(o.data_ptr(), do.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                                              wsb, B, Hq, N, d, st)
         elif step == "dkdv":
-            code = lib.fa_backward_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+            code = lib.fa_backward_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
                                         workspace.data_ptr(), wsb, dk.data_ptr(), dv.data_ptr(),
                                         B, Hq, Hkv, N, d, int(causal), float(scale), st)
         elif step == "dq":
-            code = lib.fa_backward_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+            code = lib.fa_backward_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
                                       workspace.data_ptr(), wsb, dq.data_ptr(),
                                       B, Hq, Hkv, N, d, int(causal), float(scale), st)
         else:

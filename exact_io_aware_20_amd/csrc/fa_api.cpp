@@ -13,9 +13,10 @@ constexpr long long kMaxGrid = 0x7fffffffLL;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Two fp32 per query row: D (dO . O) and LSE in base-2 units.
 size_t workspace_bytes(int B, int Hq, int N) {
     if (B < 1 || Hq < 1 || N < 1) return 0;
-    return (size_t)B * Hq * N * sizeof(float);
+    return (size_t)B * Hq * N * 2 * sizeof(float);
 }
 
 fa_status check_shape(int B, int Hq, int Hkv, int N, int d, int causal, float scale) {
@@ -83,12 +84,14 @@ fa_status check_bwd(BwdStep step, const void* q, const void* k, const void* v, c
     int n = 0;
     a[n++] = {dO, qb, false};
     a[n++] = {workspace, ws_need, step == kAll || step == kPre};
-    if (step == kAll || step == kPre) a[n++] = {o, qb, false};
+    if (step == kAll || step == kPre) {
+        a[n++] = {o, qb, false};
+        a[n++] = {lse, lb, false};
+    }
     if (step != kPre) {
         a[n++] = {q, qb, false};
         a[n++] = {k, kb, false};
         a[n++] = {v, kb, false};
-        a[n++] = {lse, lb, false};
     }
     if (step == kAll || step == kDq) a[n++] = {dq, qb, true};
     if (step == kAll || step == kDkdv) {
@@ -140,6 +143,7 @@ fa::BwdParams bwd_params(const void* q, const void* k, const void* v, const void
     p.dk = dk;
     p.dv = dv;
     p.dsum = (float*)workspace;
+    p.lse2 = (float*)workspace + (size_t)B * Hq * N;
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
@@ -189,35 +193,35 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
     return launched(fa::launch_bwd_dq(p, d, stream));
 }
 
-fa_status fa_backward_preprocess(const void* o, const void* dO, void* workspace, size_t workspace_bytes, int B,
-                                 int Hq, int N, int d, hipStream_t stream) {
-    fa_status s = check_bwd(kPre, nullptr, nullptr, nullptr, o, dO, nullptr, nullptr, nullptr, nullptr,
+fa_status fa_backward_preprocess(const void* o, const void* dO, const float* lse, void* workspace,
+                                 size_t workspace_bytes, int B, int Hq, int N, int d, hipStream_t stream) {
+    fa_status s = check_bwd(kPre, nullptr, nullptr, nullptr, o, dO, lse, nullptr, nullptr, nullptr,
                             workspace, workspace_bytes, B, Hq, Hq, N, d, 0, 1.f);
     if (s != FA_OK) return s;
-    const fa::BwdParams p = bwd_params(nullptr, nullptr, nullptr, o, dO, nullptr, nullptr, nullptr, nullptr,
+    const fa::BwdParams p = bwd_params(nullptr, nullptr, nullptr, o, dO, lse, nullptr, nullptr, nullptr,
                                        workspace, B, Hq, Hq, N, 0, 1.f);
     return launched(fa::launch_bwd_pre(p, d, stream));
 }
 
-fa_status fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                           const void* workspace, size_t workspace_bytes, void* dk, void* dv, int B, int Hq,
-                           int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
-    fa_status s = check_bwd(kDkdv, q, k, v, nullptr, dO, lse, nullptr, dk, dv, workspace, workspace_bytes, B,
+fa_status fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
+                           size_t workspace_bytes, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+                           int causal, float scale, hipStream_t stream) {
+    fa_status s = check_bwd(kDkdv, q, k, v, nullptr, dO, nullptr, nullptr, dk, dv, workspace, workspace_bytes, B,
                             Hq, Hkv, N, d, causal, scale);
     if (s != FA_OK) return s;
     const fa::BwdParams p =
-        bwd_params(q, k, v, nullptr, dO, lse, nullptr, dk, dv, workspace, B, Hq, Hkv, N, causal, scale);
+        bwd_params(q, k, v, nullptr, dO, nullptr, nullptr, dk, dv, workspace, B, Hq, Hkv, N, causal, scale);
     return launched(fa::launch_bwd_dkdv(p, d, stream));
 }
 
-fa_status fa_backward_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse,
-                         const void* workspace, size_t workspace_bytes, void* dq, int B, int Hq, int Hkv, int N,
-                         int d, int causal, float scale, hipStream_t stream) {
-    fa_status s = check_bwd(kDq, q, k, v, nullptr, dO, lse, dq, nullptr, nullptr, workspace, workspace_bytes, B,
+fa_status fa_backward_dq(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
+                         size_t workspace_bytes, void* dq, int B, int Hq, int Hkv, int N, int d, int causal,
+                         float scale, hipStream_t stream) {
+    fa_status s = check_bwd(kDq, q, k, v, nullptr, dO, nullptr, dq, nullptr, nullptr, workspace, workspace_bytes, B,
                             Hq, Hkv, N, d, causal, scale);
     if (s != FA_OK) return s;
     const fa::BwdParams p =
-        bwd_params(q, k, v, nullptr, dO, lse, dq, nullptr, nullptr, workspace, B, Hq, Hkv, N, causal, scale);
+        bwd_params(q, k, v, nullptr, dO, nullptr, dq, nullptr, nullptr, workspace, B, Hq, Hkv, N, causal, scale);
     return launched(fa::launch_bwd_dq(p, d, stream));
 }
 

@@ -11,15 +11,20 @@
 //   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
 //
 // gfx950 mapping:
-//   * dK/dV kernel: a workgroup owns 128 keys of one KV head (32 per wave, K and
-//     V held in registers) and streams 64-row tiles of Q and dO of every query
-//     head in the group through LDS (natural and transposed copies).  S = Q K^T
-//     is formed with the query on the C rows, so P and dS feed the dV and dK
-//     contractions straight from registers; the group sum over query heads
-//     happens in the accumulators (no atomics, bit-reproducible).
-//   * dQ kernel: a workgroup owns 32*QB query rows per wave of one query head
-//     (Q, dO, LSE, D in registers) and streams K/V tiles like the forward;
-//     S^T = K Q^T keeps each lane on one query, so LSE and D are lane-local.
+//   * preprocess: per query row, D = dO . O and LSE in base-2 units, written to the
+//     workspace that the other two kernels read.
+//   * dK/dV kernel: a workgroup owns 128 keys of one KV head; waves 0-3 accumulate
+//     dK and waves 4-7 dV for 32 keys each (K, V in registers), streaming 64-row
+//     tiles of Q and dO of every query head in the group through LDS by direct
+//     loads.  S = Q K^T is formed with the query on the C rows, so P and dS feed
+//     the dV and dK contractions straight from registers; the Q^T and dO^T
+//     operands of those contractions come from the same natural tiles through the
+//     transposing LDS read.  The group sum over query heads happens in the
+//     accumulators (no atomics, bit-reproducible).
+//   * dQ kernel: a workgroup owns 32 query rows per wave of one query head (Q, dO,
+//     LSE, D in registers) and streams K/V tiles like the forward; S^T = K Q^T
+//     keeps each lane on one query, so LSE and D are lane-local, and the K^T
+//     operand of dQ^T += K^T dS^T is read transposed from the natural K tile.
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -29,11 +34,13 @@ __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x 
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
 // ---------------------------------------------------------------------------------
-// D_i = sum_t dO_it * O_it (fp32), D/8 lanes per row, 16 bytes per lane.
+// Per query row: D_i = sum_t dO_it * O_it (fp32) and LSE_i * log2(e).  D/8 lanes
+// per row, 16 bytes per lane.
 // ---------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void fa_bwd_pre_kernel(const uint16_t* o, const uint16_t* dO,
-                                                              float* dsum, long long rows) {
+                                                              const float* lse, float* dsum, float* lse2,
+                                                              long long rows) {
     constexpr int LPR = D / 8;
     const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
     const long long row = gid / LPR;
@@ -51,6 +58,7 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_pre_kernel(const uint16_t* o,
 #pragma unroll
     for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
     if (row < rows && sub == 0) dsum[row] = acc;
+    if (row < rows && sub == 1) lse2[row] = lse[row] * kLog2e;
 }
 
 // ---------------------------------------------------------------------------------
@@ -64,10 +72,8 @@ struct DkdvCfg {
     static constexpr int BQ = 64;            // query rows per streamed tile
     static constexpr int DC = D / 16;
     static constexpr int DB = D / 32;
-    static constexpr int NAT = SwzTile<D, 1>::ELEMS;   // natural Q or dO tile
-    static constexpr int TR = PermT<D>::ELEMS;         // transposed Q or dO tile
-    static constexpr int NSTAGE = 2 * NAT;             // natural Q, dO (double-buffered)
-    static constexpr int TSTAGE = 2 * TR + 2 * 64 * 2; // transposed Q, dO; LSE*log2e, D (fp32)
+    static constexpr int NAT = SwzTile<D, 1>::ELEMS;   // natural Q or dO tile (bf16 elements)
+    static constexpr int STAGE = 2 * NAT + 2 * BQ * 2;  // Q, dO, then LSE2 and D (fp32, BQ each)
 };
 
 // C[q][key] = sum_d A[q][d] B[key][d] for query half qb (32 rows) of a natural
@@ -92,11 +98,12 @@ __device__ __forceinline__ void mask_half(f32x16& s, int qrow0, int key, int N, 
 }
 
 // One query half: P = 2^(S*sl2 - LSE2); dK waves form dS = P (dP - D) and
-// accumulate dK^T += Q^T dS, dV waves accumulate dV^T += dO^T P.  Register 4g+i
-// of a C tile is k-slot 4(g%2)+i of fragment g/2 (query 8g + 4hh + i of the half).
+// accumulate dK^T += Q^T dS, dV waves accumulate dV^T += dO^T P, the A operand
+// (`tt`: Q or dO tile) read transposed.  Register 4g+i of a C tile is k-slot
+// 4(g%2)+i of fragment g/2 (query 8g + 4hh + i of the half).
 template <int D, bool DK>
-__device__ __forceinline__ void grads_half(const f32x16& s, const f32x16& dp, const uint16_t* tr, const float* lse2,
-                                           const float* dvec, f32x16 (&acc)[D / 32], float sl2, int qb, int l32,
+__device__ __forceinline__ void grads_half(const f32x16& s, const f32x16& dp, const uint16_t* tt, const float* lse2,
+                                           const float* dvec, f32x16 (&acc)[D / 32], float sl2, int qb, int lane,
                                            int hh) {
     u32x4 bf[2];
 #pragma unroll
@@ -117,29 +124,20 @@ __device__ __forceinline__ void grads_half(const f32x16& s, const f32x16& dp, co
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
-            acc[db] = mfma32x32x16(permt_frag<D>(tr, 32 * db + l32, 32 * qb + 16 * h2, hh), bf[h2], acc[db]);
+            acc[db] = mfma32x32x16(tr_frag<D>(tt, db, 32 * qb + 16 * h2, lane), bf[h2], acc[db]);
 }
 
 // dK/dV kernel.  A workgroup owns 128 keys of one KV head; waves 0-3 accumulate
 // dK and waves 4-7 dV for keys 32(w%4) .. +31, so each wave holds one accumulator
-// set and two waves fit per SIMD (the dK and dV waves of a key block share one).
-// Both recompute S; the dK wave also forms dP.  64-row query tiles of every query
-// head of the group stream through LDS.  Iteration it:
-//   A. wait for this wave's loads of item it, barrier;
-//   B. direct loads of item it+1 (natural Q, dO) into the other buffer, LSE/D;
-//   C. transposed, permuted Q and dO of item it built in LDS (one 4x8 item per thread);
-//   D. S (and dP) of the first query half; barrier;
-//   E. gradients of the first half while S (and dP) of the second half run on the
-//      matrix cores, then the gradients of the second half.
+// set and two waves fit per SIMD.  Both recompute S; the dK wave also forms dP.
+// Items are (query head of the group, 64-row query tile); item it's Q and dO tiles
+// and its LSE2/D vectors sit in stage it&1 of LDS, all filled by direct loads.
+// Iteration it: wait for item it's loads and a workgroup barrier (so stage
+// (it+1)&1, last used by item it-1, is free), issue item it+1's loads into it,
+// then compute item it.
 template <int D, bool DK>
-__device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, int tid, int wave, int lane) {
+__device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, int wave, int lane) {
     using C = DkdvCfg<D>;
-    constexpr int NS = C::NSTAGE;
-    uint16_t* nat = smem;              // item it: natural Q at nat + (it&1)*NS, dO at + NAT
-    uint16_t* trs = smem + 2 * NS;     // transposed Q, dO, then LSE*log2e and D of the current item
-    float* vec = (float*)(trs + 2 * C::TR);
-    const uint16_t* my_tr = trs + (DK ? 0 : C::TR);
-
     const int l32 = lane & 31;
     const int hh = lane >> 5;
     const int N = p.N;
@@ -172,46 +170,41 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, in
     const int nitems = G * per_head;
     const float sl2 = p.scale_log2;
 
-    float vec_reg = 0.f;
+    TileDma<D, 1, C::WAVES> dma;
+    dma.init(wave, lane);
     auto issue_item = [&](int it) {
         const int hq = hkv * G + it / per_head;
         const int q0 = (qt_start + it % per_head) * C::BQ;
-        const size_t qoff = ((size_t)(b * p.Hq + hq) * N + q0) * D;
-        uint16_t* st = nat + (it & 1) * NS;
-        swz_tile_issue<D, 1, C::WAVES>((const uint16_t*)p.q + qoff, N - q0, st, wave, lane);
-        swz_tile_issue<D, 1, C::WAVES>((const uint16_t*)p.dO + qoff, N - q0, st + C::NAT, wave, lane);
         const size_t roff = (size_t)(b * p.Hq + hq) * N + q0;
-        if (tid < 64) vec_reg = q0 + tid < N ? p.lse[roff + tid] * kLog2e : 0.f;
-        else if (tid < 128) vec_reg = q0 + tid - 64 < N ? p.dsum[roff + tid - 64] : 0.f;
+        uint16_t* st = smem + (it & 1) * C::STAGE;
+        dma.issue((const uint16_t*)p.q + roff * D, N - q0, st, wave);
+        dma.issue((const uint16_t*)p.dO + roff * D, N - q0, st + C::NAT, wave);
+        // LSE2 (wave 0) and D (wave 1): 4 bytes per lane; rows >= N read row N-1
+        if (wave < 2) {
+            const float* src = (wave == 0 ? p.lse2 : p.dsum) + roff + min(lane, N - 1 - q0);
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(st + 2 * C::NAT + wave * 2 * C::BQ), 4, 0, 0);
+        }
     };
 
     if (nitems > 0) issue_item(0);
     for (int it = 0; it < nitems; ++it) {
         const int q0 = (qt_start + it % per_head) * C::BQ;
-        const uint16_t* nb = nat + (it & 1) * NS;
+        const uint16_t* st = smem + (it & 1) * C::STAGE;
+        const float* lse2 = (const float*)(st + 2 * C::NAT);
+        const float* dvec = lse2 + C::BQ;
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();                                            // A
-        if (tid < 128) vec[tid] = vec_reg;
-        if (it + 1 < nitems) issue_item(it + 1);                    // B
-        {                                                           // C
-            const int which = tid / PermT<D>::ITEMS;                // 0: Q, 1: dO
-            if (which < 2) permt_from_lds<D, 1>(nb + which * C::NAT, trs + which * C::TR, N - q0, tid % PermT<D>::ITEMS);
-        }
+        __syncthreads();
+        if (it + 1 < nitems) issue_item(it + 1);
         const bool act = kw0 < N && (!p.causal || q0 + C::BQ - 1 >= kw0);
         const bool mask = (p.causal && q0 < kw0 + 31) || (q0 + C::BQ > N);
-        f32x16 s0, d0 = zero16();
-        if (act) {                                                  // D
-            s0 = qk_half<D>(nb, kf, 0, l32, hh);
-            if constexpr (DK) d0 = qk_half<D>(nb + C::NAT, vf, 0, l32, hh);
-        }
-        __syncthreads();
-        if (act) {                                                  // E
-            if (mask) mask_half(s0, q0 + 4 * hh, key, N, p.causal);
-            grads_half<D, DK>(s0, d0, my_tr, vec, vec + 64, acc, sl2, 0, l32, hh);
-            f32x16 s1 = qk_half<D>(nb, kf, 1, l32, hh), d1 = zero16();
-            if constexpr (DK) d1 = qk_half<D>(nb + C::NAT, vf, 1, l32, hh);
-            if (mask) mask_half(s1, q0 + 32 + 4 * hh, key, N, p.causal);
-            grads_half<D, DK>(s1, d1, my_tr, vec, vec + 64, acc, sl2, 1, l32, hh);
+        if (act) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                f32x16 s = qk_half<D>(st, kf, qb, l32, hh), dp = zero16();
+                if constexpr (DK) dp = qk_half<D>(st + C::NAT, vf, qb, l32, hh);
+                if (mask) mask_half(s, q0 + 32 * qb + 4 * hh, key, N, p.causal);
+                grads_half<D, DK>(s, dp, st + (DK ? 0 : C::NAT), lse2, dvec, acc, sl2, qb, lane, hh);
+            }
         }
     }
 
@@ -231,13 +224,14 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, in
 template <int D>
 __global__ __launch_bounds__(DkdvCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * DkdvCfg<D>::NSTAGE + DkdvCfg<D>::TSTAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * DkdvCfg<D>::STAGE];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(wave < DkdvCfg<D>::WAVES);
     if (wave < 4)
-        dkdv_role<D, true>(p, smem, tid, wave, tid & 63);
+        dkdv_role<D, true>(p, smem, wave, tid & 63);
     else
-        dkdv_role<D, false>(p, smem, tid, wave, tid & 63);
+        dkdv_role<D, false>(p, smem, wave, tid & 63);
 }
 
 // ---------------------------------------------------------------------------------
@@ -251,21 +245,26 @@ struct DqCfg {
     static constexpr int BC = 64;
     static constexpr int DC = D / 16;
     static constexpr int DB = D / 32;
-    static constexpr int NAT = SwzTile<D, 0>::ELEMS;
-    static constexpr int TR = PermT<D>::ELEMS;
-    static constexpr int STAGE = 2 * NAT + TR;   // K natural, V natural, K transposed
+    static constexpr int KT = SwzTile<D, 1>::ELEMS;   // K: fragment and transposing reads
+    static constexpr int VT = SwzTile<D, 0>::ELEMS;   // V: fragment reads
+    static constexpr int STAGE = KT + VT;
 };
 
+// dQ kernel: per key/value tile, S^T = K Q^T and dP^T = V dO^T (lane: query),
+// dS^T = P^T (dP^T - D) rounded to bf16, dQ^T += K^T dS^T with K^T read transposed
+// from the natural K tile.  K/V tiles are double-buffered with one barrier each.
 template <int D>
 __global__ __launch_bounds__(DqCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(BwdParams p) {
     using C = DqCfg<D>;
-    using NT = SwzTile<D, 0>;
+    using KS = SwzTile<D, 1>;
+    using VS = SwzTile<D, 0>;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(wave < C::WAVES);
     const int l32 = lane & 31;
     const int hh = lane >> 5;
     const int N = p.N;
@@ -297,33 +296,30 @@ void fa_bwd_dq_kernel(BwdParams p) {
         qf[c] = ok ? ld_global16((const uint16_t*)p.q + qoff + (size_t)q * D + 16 * c + 8 * hh) : zero_u4();
         gf[c] = ok ? ld_global16((const uint16_t*)p.dO + qoff + (size_t)q * D + 16 * c + 8 * hh) : zero_u4();
     }
-    const float lse2 = ok ? p.lse[(size_t)head * N + q] * kLog2e : 0.f;
+    const float lse2 = ok ? p.lse2[(size_t)head * N + q] : 0.f;
     const float dd = ok ? p.dsum[(size_t)head * N + q] : 0.f;
     f32x16 dqt[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) dqt[db] = zero16();
     const float sl2 = p.scale_log2;
 
-    const bool stager = tid < PermT<D>::ITEMS;
-    u32x4 kr[4];
+    TileDma<D, 1, C::WAVES> kdma;
+    TileDma<D, 0, C::WAVES> vdma;
+    kdma.init(wave, lane);
+    vdma.init(wave, lane);
     auto load_tile = [&](int t, uint16_t* st) {
         const int k0 = t * C::BC;
-        swz_tile_issue<D, 0, C::WAVES>(Kh + (size_t)k0 * D, N - k0, st, wave, lane);
-        swz_tile_issue<D, 0, C::WAVES>(Vh + (size_t)k0 * D, N - k0, st + C::NAT, wave, lane);
-        if (stager) permt_load<D>(kr, Kh + (size_t)k0 * D, N - k0, tid);
+        kdma.issue(Kh + (size_t)k0 * D, N - k0, st, wave);
+        vdma.issue(Vh + (size_t)k0 * D, N - k0, st + C::KT, wave);
     };
 
     load_tile(0, smem);
-    if (stager) permt_store<D>(kr, smem + 2 * C::NAT, tid);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
     for (int t = 0; t < ntiles; ++t) {
         const int k0 = t * C::BC;
-        const bool more = t + 1 < ntiles;
-        uint16_t* nb = smem + ((t + 1) & 1) * C::STAGE;
-        if (more) load_tile(t + 1, nb);
         const uint16_t* st = smem + (t & 1) * C::STAGE;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();                       // tile t landed; stage (t+1)&1 free
+        if (t + 1 < ntiles) load_tile(t + 1, smem + ((t + 1) & 1) * C::STAGE);
 
         if (t < wave_tiles) {
             f32x16 s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
@@ -331,8 +327,8 @@ void fa_bwd_dq_kernel(BwdParams p) {
             for (int c = 0; c < C::DC; ++c)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    s[kb] = mfma32x32x16(lds16(st + NT::at(32 * kb + l32, 2 * c + hh)), qf[c], s[kb]);
-                    dp[kb] = mfma32x32x16(lds16(st + C::NAT + NT::at(32 * kb + l32, 2 * c + hh)), gf[c], dp[kb]);
+                    s[kb] = mfma32x32x16(lds16(st + KS::at(32 * kb + l32, 2 * c + hh)), qf[c], s[kb]);
+                    dp[kb] = mfma32x32x16(lds16(st + C::KT + VS::at(32 * kb + l32, 2 * c + hh)), gf[c], dp[kb]);
                 }
             if ((p.causal && k0 + C::BC - 1 > qw0) || (k0 + C::BC > N)) {
 #pragma unroll
@@ -363,13 +359,8 @@ void fa_bwd_dq_kernel(BwdParams p) {
                 for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
                     for (int db = 0; db < C::DB; ++db)
-                        dqt[db] = mfma32x32x16(permt_frag<D>(st + 2 * C::NAT, 32 * db + l32, 32 * kb + 16 * h2, hh),
-                                               dsf[kb][h2], dqt[db]);
+                        dqt[db] = mfma32x32x16(tr_frag<D>(st, db, 32 * kb + 16 * h2, lane), dsf[kb][h2], dqt[db]);
         }
-
-        if (more && stager) permt_store<D>(kr, nb + 2 * C::NAT, tid);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
     }
 
     if (ok) {
@@ -401,7 +392,7 @@ static hipError_t launch_pre(const BwdParams& p, hipStream_t stream) {
     const long long rows = (long long)p.B * p.Hq * p.N;
     const unsigned blocks = (unsigned)((rows * (D / 8) + kThreads - 1) / kThreads);
     hipLaunchKernelGGL(fa_bwd_pre_kernel<D>, dim3(blocks), dim3(kThreads), 0, stream,
-                       (const uint16_t*)p.o, (const uint16_t*)p.dO, p.dsum, rows);
+                       (const uint16_t*)p.o, (const uint16_t*)p.dO, p.lse, p.dsum, p.lse2, rows);
     return hipGetLastError();
 }
 

@@ -86,17 +86,22 @@ __device__ __forceinline__ void map_block(int bid, int nblk, int ntile, int nhea
 // (global_load_lds_dwordx4: lane L of a wave writes 16 bytes at base + 16*L).
 // Row r's 16-byte chunk j lives at slot j ^ swz(r), with no padding.
 //
-// ds_read_b128 serves a wave in four cycles of 16 lanes: the lanes of one half
-// (l / 32) whose bits 2..4 have equal parity (measured on gfx950 with the
-// SQ_LDS_BANK_CONFLICT counter, one pair of active lanes at a time).  A cycle is
-// conflict-free when its 16 lanes touch 16 distinct 16-byte slots of a 256-byte
-// bank window.  The swizzles are chosen for that grouping:
-//   MODE 0: fragment reads (lane l: row 32q + l%32, chunk 2k + l/32);
-//   MODE 1: fragment reads and transposing reads (lane l of a wave: rows 4(l%16)+j
-//           of chunk c0 + l/16).  For D = 128 the Gray code r ^ r/2 serves both
-//           with no conflict; for D = 64 (two rows per bank window) the rows of a
-//           transposing read share a parity, so a 2-way conflict there is the
-//           least any row swizzle allows, and r ^ r/4 reaches it.
+// Two read patterns touch these tiles (bank = 4-byte word index mod 64):
+//  * row fragments, ds_read_b128: lane l reads row 32q + l%32, chunk 2k + l/32.
+//    The wave is served in four cycles of 16 lanes: the lanes of one half (l/32)
+//    whose bits 2..4 have equal parity (measured on gfx950 with the
+//    SQ_LDS_BANK_CONFLICT counter, one pair of active lanes at a time).  A cycle
+//    is conflict-free when its lanes touch 16 distinct 16-byte slots of a
+//    256-byte bank window.
+//  * transposing reads, ds_read_b64_tr_b16 (tr_frag below): each half-wave cycle
+//    reads 4 consecutive rows (aligned to 4) x 4 consecutive chunks (aligned to 4).
+//    Conflict-free when the four rows put that 64-byte unit in four different
+//    units of the bank window.
+//   MODE 0 serves the fragment pattern only (r mod 16 for D = 128, two rows per
+//   window for D = 64); MODE 1 serves both with a bit permutation of the row:
+//   D = 128: bits (1,0 | 3,2) of r -> chunk bits (3,2 | 1,0); D = 64: r bits
+//   1, 2, 3 -> chunk bits 2, 1, 0.  Both checked exhaustively on the CPU against
+//   the cycle grouping above.
 // ---------------------------------------------------------------------------------
 template <int D, int MODE = 0>
 struct SwzTile {
@@ -105,7 +110,7 @@ struct SwzTile {
     static constexpr int WAVE_LOADS = 64 * CHUNKS / kWave;   // wave-instructions per tile
     __device__ static __forceinline__ int swz(int r) {
         if (MODE == 0) return D == 128 ? (r & 15) : ((r >> 1) & 7);
-        return D == 128 ? ((r ^ (r >> 1)) & 15) : ((r ^ (r >> 2)) & 7);
+        return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : (((r & 2) << 1) | ((r >> 1) & 2) | ((r >> 3) & 1));
     }
     // element offset of (row, chunk)
     __device__ static __forceinline__ int at(int r, int j) { return r * D + ((j ^ swz(r)) << 3); }
@@ -148,72 +153,62 @@ __device__ __forceinline__ int swz_tile_issue(const uint16_t* src, int nvalid, u
     return issued;
 }
 
-// ---------------------------------------------------------------------------------
-// Transposed tile with key-permuted columns: [D][64 + 8] bf16.  Column position of
-// key k within its 16-key block: 8*((k/4)&1) + 4*((k/8)&1) + (k%4), so that the 8
-// keys one lane feeds to a 32x32x16 MFMA (k-slot order 4h+{0..3}, 8+4h+{0..3}) are
-// contiguous and a fragment is one 16-byte read.
-// ---------------------------------------------------------------------------------
-template <int D>
-struct PermT {
-    static constexpr int STR = 64 + 8;
-    static constexpr int ELEMS = D * STR;
-    static constexpr int ITEMS = (D / 8) * 16;   // 4 keys x 8 columns per item
+// The same loads with the per-lane source offsets computed once: a wave's chunk
+// positions in the tile do not change from tile to tile, so issuing a tile costs
+// a clamp and an address add per load.  `wave` must be below NWAVES.
+template <int D, int MODE, int NWAVES>
+struct TileDma {
+    using S = SwzTile<D, MODE>;
+    static constexpr int PER = (S::WAVE_LOADS + NWAVES - 1) / NWAVES;
+    int off[PER];   // element offset of this lane's 16-byte chunk within the global tile
+    int row[PER];   // its tile row
+    __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int pos = (wave + k * NWAVES) * 64 + lane;
+            row[k] = pos / S::CHUNKS;
+            off[k] = row[k] * D + ((pos % S::CHUNKS) ^ S::swz(row[k])) * 8;
+        }
+    }
+    // rows at or past `nvalid` are read from row nvalid-1 (in bounds, never used)
+    __device__ __forceinline__ void issue(const uint16_t* src, int nvalid, uint16_t* lds_tile, int wave) const {
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = wave + k * NWAVES;
+            if (S::WAVE_LOADS % NWAVES == 0 || i < S::WAVE_LOADS) {
+                const int o = off[k] + (min(row[k], nvalid - 1) - row[k]) * D;
+                __builtin_amdgcn_global_load_lds(src + o, (lds_void*)(lds_tile + i * 64 * 8), 16, 0, 0);
+            }
+        }
+    }
 };
 
-__device__ __forceinline__ int perm_pos4(int kq) {   // position of key 4*kq
-    return 16 * (kq >> 2) + 8 * (kq & 1) + 4 * ((kq >> 1) & 1);
+// ---------------------------------------------------------------------------------
+// A-operand fragment of X^T (D x 64) read from a natural MODE 1 tile X [64][D] with
+// two ds_read_b64_tr_b16.  That instruction works on groups of 16 lanes: lane m of
+// a group supplies the address of 4 consecutive bf16, and lane 4a+p receives
+// element p of the values addressed by lanes a, a+4, a+8, a+12.  Lane m of group
+// g = l/16 addresses row kk + 4(g/2) + m/4 (+8 for the second read), columns
+// 32db + 16(g%2) + 4(m%4) .. +3, so lane l receives column d = 32db + l%32 of the 8
+// rows kk + {4h .. 4h+3, 8+4h .. 8+4h+3}, h = l/32: the k-slot order in which a
+// C tile's registers feed a B operand (see the convention at the top).
+// ---------------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ u32x2 tr_read(const uint16_t* p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
 }
 
-// Items are numbered key-quad fastest: the 16 lanes of a store cover one row's 64
-// keys, so a wave's eight-byte stores hit distinct banks.
 template <int D>
-__device__ __forceinline__ void permt_load(u32x4 (&r)[4], const uint16_t* src, int nvalid, int item) {
-    const int kq = item % 16, c = item / 16;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = kq * 4 + j;
-        r[j] = row < nvalid ? ld_global16(src + (size_t)row * D + c * 8) : zero_u4();
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void permt_store(const u32x4 (&r)[4], uint16_t* dst, int item) {
-    const int kq = item % 16, c = item / 16;
-    const int col = perm_pos4(kq);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        const uint32_t a = r[0][w], b = r[1][w], cc = r[2][w], d = r[3][w];
-        const u32x2 even = {(a & 0xffffu) | (b << 16), (cc & 0xffffu) | (d << 16)};
-        const u32x2 odd = {(a >> 16) | (b & 0xffff0000u), (cc >> 16) | (d & 0xffff0000u)};
-        *(u32x2*)(dst + (c * 8 + 2 * w) * PermT<D>::STR + col) = even;
-        *(u32x2*)(dst + (c * 8 + 2 * w + 1) * PermT<D>::STR + col) = odd;
-    }
-}
-
-// Transpose one item (4 rows x 8 columns) from a MODE 1 swizzled natural tile in
-// LDS into the permuted transposed layout.  Rows >= nvalid are written as zero, so
-// stale or clamped rows contribute nothing to the contractions over rows.
-template <int D, int MODE = 1>
-__device__ __forceinline__ void permt_from_lds(const uint16_t* src, uint16_t* dst, int nvalid, int item) {
-    using S = SwzTile<D, MODE>;
-    item = opaque(item);
-    const int kq = item % 16, c = item / 16;
-    u32x4 r[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = kq * 4 + j;
-        r[j] = lds16(src + S::at(row, c));
-        if (row >= nvalid) r[j] = zero_u4();
-    }
-    permt_store<D>(r, dst, item);
-}
-
-// Fragment of the permuted transposed tile: row `row` (an index into d), the 8
-// keys kk + {4h..4h+3, 8+4h..8+4h+3} (kk a multiple of 16).
-template <int D>
-__device__ __forceinline__ u32x4 permt_frag(const uint16_t* base, int row, int kk, int half) {
-    return lds16(base + row * PermT<D>::STR + kk + 8 * half);
+__device__ __forceinline__ u32x4 tr_frag(const uint16_t* tile, int db, int kk, int lane) {
+    using S = SwzTile<D, 1>;
+    const int g = lane >> 4, m = lane & 15;
+    const int row = kk + 4 * (g >> 1) + (m >> 2);
+    const int col = 32 * db + 16 * (g & 1) + 4 * (m & 3);
+    const u32x2 lo = tr_read(tile + S::at(row, col >> 3) + (col & 7));
+    const u32x2 hi = tr_read(tile + S::at(row + 8, col >> 3) + (col & 7));
+    return cat(lo, hi);
 }
 
 }  // namespace fa

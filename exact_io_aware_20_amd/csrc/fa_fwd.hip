@@ -12,14 +12,14 @@
 // gfx950 mapping of the bf16 kernel:
 //   * 8 waves per workgroup (two per SIMD, so one wave's softmax overlaps the
 //     other's matrix work), each owning 32 query rows.  K/V tiles of 64 keys are
-//     double-buffered in LDS with one barrier per tile: K arrives by direct
-//     global->LDS loads into an XOR-swizzled layout, V through registers into a
-//     transposed, key-permuted layout whose fragments are single 16-byte reads.
+//     double-buffered in LDS with one barrier per tile; both arrive by direct
+//     global->LDS loads into XOR-swizzled natural layouts (no register staging).
 //   * Scores are formed transposed, S^T = K Q^T, so a lane holds one query (its
 //     column) and 16 keys; the row maximum is an in-lane max plus one exchange
 //     with lane l^32, and the running statistics are lane-local scalars.
 //   * O^T = V^T P^T reuses the S^T registers, rounded to bf16, directly as the
-//     B operand; V is staged transposed in LDS for the A operand.
+//     B operand; the V^T A operand is read from the natural V tile with the
+//     transposing LDS read (two 8-byte reads per fragment).
 //   * Scores are kept in base-2 units (scale*log2 e folded into one FMA before
 //     v_exp_f32).  The reference maximum is only moved when a row's maximum
 //     grows by more than 2^8 (kRescaleLog2): the quotient O = sum p v / sum p is
@@ -72,23 +72,24 @@ __device__ __forceinline__ float pair_max(float x) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Online-softmax update of one tile's scores and O^T += V^T P^T.  `mask`
-// (wave-uniform) applies the causal diagonal and keys >= N.
+// Causal diagonal and keys >= N: masked scores become -inf (p = 0).
+__device__ __forceinline__ void fwd_mask(f32x16 (&s)[2], int k0, int q, int N, int causal, int hh) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const bool vis = key < N && (!causal || key <= q);
+            s[kb][r] = vis ? s[kb][r] : kNegInf;
+        }
+}
+
+// Row max (in-lane chain, then the partner lane) and the lazy rescale: the
+// reference m_ref (base-2 units) moves only when the row maximum exceeds it by
+// more than kRescaleLog2; O and l are then multiplied by 2^(m_old - m_new).
 template <int D>
-__device__ __forceinline__ void fwd_softmax_pv(f32x16 (&s)[2], const uint16_t* Vt, f32x16 (&o)[D / 32],
-                                               float& m_ref, float& l_part, float sl2, int k0, int q, int N,
-                                               int causal, int l32, int hh, bool mask) {
-    if (mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const bool vis = key < N && (!causal || key <= q);
-                s[kb][r] = vis ? s[kb][r] : kNegInf;
-            }
-    }
-    // row max: in-lane max3 chain, then the partner lane; lazy rescale
+__device__ __forceinline__ void fwd_rescale(const f32x16 (&s)[2], f32x16 (&o)[D / 32], float& m_ref, float& l_part,
+                                            float sl2) {
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -107,10 +108,13 @@ __device__ __forceinline__ void fwd_softmax_pv(f32x16 (&s)[2], const uint16_t* V
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
-    // P = 2^(S*sl2 - m) (masked scores are -inf: p = 0), packed to bf16 as the
-    // B operand of O^T = V^T P^T; l accumulates the same rounded values
+}
+
+// P = 2^(S*sl2 - m_ref), rounded to bf16 and packed as the B operand of
+// O^T = V^T P^T; l accumulates the same rounded values.
+__device__ __forceinline__ void fwd_probs(const f32x16 (&s)[2], float m_ref, float sl2, u32x4 (&pf)[2][2],
+                                          float& l_part) {
     const float mref = m_ref == kNegInf ? 0.f : m_ref;
-    u32x4 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -123,28 +127,34 @@ __device__ __forceinline__ void fwd_softmax_pv(f32x16 (&s)[2], const uint16_t* V
                 pf[kb][h2][j] = pk;
                 l_part = add_bf16_pair(pk, l_part);
             }
+}
+
+// O^T += V^T P^T over the tile's 64 keys (A operand read transposed from the
+// natural V tile).
+template <int D>
+__device__ __forceinline__ void fwd_pv(const uint16_t* Vt, const u32x4 (&pf)[2][2], f32x16 (&o)[D / 32], int lane) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const u32x4 vf = permt_frag<D>(Vt, 32 * db + l32, 32 * kb + 16 * h2, hh);
-                o[db] = mfma32x32x16(vf, pf[kb][h2], o[db]);
-            }
+            for (int db = 0; db < D / 32; ++db)
+                o[db] = mfma32x32x16(tr_frag<D>(Vt, db, 32 * kb + 16 * h2, lane), pf[kb][h2], o[db]);
 }
 
-// The kernel is software-pipelined by one tile: S(t+1) = K(t+1) Q^T is issued
-// to the matrix cores before the softmax of tile t, so the two can overlap.  LDS
-// holds K(t+1) and V(t) during iteration t; K(t+2) (direct loads) and V(t+1)
-// (through registers, transposed on the way) are written into the other halves
-// of the two double buffers meanwhile, one workgroup barrier per iteration.
+// The kernel is software-pipelined by one tile: S(t+1) = K(t+1) Q^T goes to the
+// matrix cores while the vector units turn S(t) into probabilities.  LDS holds
+// K(t+1) and V(t) during step t; the direct loads of K(t+2) and V(t+1) fill the
+// other halves of the two double buffers meanwhile, one workgroup barrier per step.
+// The leading steps, whose current and next tiles are fully visible to every row
+// of the workgroup, run as branch-free blocks in a loop of their own; the
+// diagonal and ragged tail steps take the general path.
 template <int D>
 __global__ __launch_bounds__(FwdCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_kernel(FwdParams p) {
     using C = FwdCfg<D>;
     constexpr int KB = SwzTile<D, 0>::ELEMS;
-    constexpr int VB = PermT<D>::ELEMS;
+    constexpr int VB = SwzTile<D, 1>::ELEMS;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * KB + 2 * VB];
     uint16_t* kbuf = smem;            // K tile of parity t&1 at kbuf + (t&1)*KB
     uint16_t* vbuf = smem + 2 * KB;   // V tile of parity t&1 at vbuf + (t&1)*VB
@@ -152,6 +162,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(wave < C::WAVES);
     const int l32 = lane & 31;
     const int hh = lane >> 5;
     const int N = p.N;
@@ -187,19 +198,16 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     float m_ref = kNegInf, l_part = 0.f;
     const float sl2 = p.scale_log2;
 
-    // V tile items (4 keys x 8 columns) are staged by the first ITEMS threads.
-    const bool v_stager = tid < PermT<D>::ITEMS;
-    u32x4 vr[4];
     auto issue_k = [&](int t, uint16_t* buf) {
         swz_tile_issue<D, 0, C::WAVES>(Kh + (size_t)t * C::BC * D, N - t * C::BC, buf, wave, lane);
+    };
+    auto issue_v = [&](int t, uint16_t* buf) {
+        swz_tile_issue<D, 1, C::WAVES>(Vh + (size_t)t * C::BC * D, N - t * C::BC, buf, wave, lane);
     };
 
     // prologue: K(0), V(0) -> LDS; S(0); K(1) -> LDS
     issue_k(0, kbuf);
-    if (v_stager) {
-        permt_load<D>(vr, Vh, N, tid);
-        permt_store<D>(vr, vbuf, tid);
-    }
+    issue_v(0, vbuf);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16 sa[2], sb[2];
@@ -208,22 +216,57 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // one pipelined step: tile t's softmax/PV with scores `cur`, tile t+1's scores into `nxt`
-    auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-        const int k0 = t * C::BC;
-        if (t + 2 < ntiles) issue_k(t + 2, kbuf + (t & 1) * KB);
-        const bool more = t + 1 < ntiles;
-        if (more && v_stager) permt_load<D>(vr, Vh + (size_t)(k0 + C::BC) * D, N - (k0 + C::BC), tid);
-        if (t + 1 < wave_tiles) fwd_scores<D>(kbuf + ((t + 1) & 1) * KB, qf, nxt, l32, hh);
-        if (t < wave_tiles) {
-            const bool mask = (p.causal && k0 + C::BC - 1 > qw0) || (k0 + C::BC > N);
-            fwd_softmax_pv<D>(cur, vbuf + (t & 1) * VB, o, m_ref, l_part, sl2, k0, q, N, p.causal, l32, hh, mask);
-        }
-        if (more && v_stager) permt_store<D>(vr, vbuf + ((t + 1) & 1) * VB, tid);
+    // Fast step: tiles t and t+1 are fully visible to every row of the workgroup
+    // (so t+1 < ntiles and V(t+1) exists; K(t+2) may not, and then the last tile
+    // is reloaded into the free buffer).  One branch-free block apart from the
+    // rare rescale, in a fixed phase order: scores(t+1) to the matrix cores, the
+    // exponentials of tile t, then PV(t) (the compiler's own interleave of these
+    // phases measured slower).
+    auto fast_step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+        fwd_rescale<D>(cur, o, m_ref, l_part, sl2);
+        issue_k(min(t + 2, ntiles - 1), kbuf + (t & 1) * KB);
+        issue_v(t + 1, vbuf + ((t + 1) & 1) * VB);
+        u32x4 pf[2][2];
+        fwd_scores<D>(kbuf + ((t + 1) & 1) * KB, qf, nxt, l32, hh);
+        __builtin_amdgcn_sched_barrier(0);
+        fwd_probs(cur, m_ref, sl2, pf, l_part);
+        __builtin_amdgcn_sched_barrier(0);
+        fwd_pv<D>(vbuf + (t & 1) * VB, pf, o, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
-    for (int t = 0; t < ntiles; t += 2) {
+    // General step (diagonal and ragged tiles): tile t's softmax/PV with scores
+    // `cur`, tile t+1's scores into `nxt`.
+    auto step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+        const int k0 = t * C::BC;
+        if (t + 2 < ntiles) issue_k(t + 2, kbuf + (t & 1) * KB);
+        if (t + 1 < ntiles) issue_v(t + 1, vbuf + ((t + 1) & 1) * VB);
+        if (t + 1 < wave_tiles) fwd_scores<D>(kbuf + ((t + 1) & 1) * KB, qf, nxt, l32, hh);
+        if (t < wave_tiles) {
+            if ((p.causal && k0 + C::BC - 1 > qw0) || (k0 + C::BC > N)) fwd_mask(cur, k0, q, N, p.causal, hh);
+            fwd_rescale<D>(cur, o, m_ref, l_part, sl2);
+            u32x4 pf[2][2];
+            fwd_probs(cur, m_ref, sl2, pf, l_part);
+            fwd_pv<D>(vbuf + (t & 1) * VB, pf, o, lane);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+    // steps 0 .. nfast-1 are fast for every wave (wave 0 has the fewest visible tiles)
+    const int full_wg = p.causal ? (q0 + 1) / C::BC : N / C::BC;
+    const int nfast = max(0, min(full_wg, ntiles) - 1);
+    int t = 0;
+    for (; t + 1 < nfast; t += 2) {
+        fast_step(t, sa, sb);
+        fast_step(t + 1, sb, sa);
+    }
+    if (t < nfast) {
+        fast_step(t, sa, sb);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
+        ++t;
+    }
+    for (; t < ntiles; t += 2) {
         step(t, sa, sb);
         if (t + 1 < ntiles) step(t + 1, sb, sa);
     }

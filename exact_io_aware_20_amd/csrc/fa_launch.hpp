@@ -27,6 +27,7 @@ struct BwdParams {
     void* dk;
     void* dv;
     float* dsum;        // workspace: D_i = dO_i . O_i, one fp32 per query row
+    float* lse2;        // workspace: LSE_i * log2(e), one fp32 per query row
     int B, Hq, Hkv, N, causal;
     float scale;
     float scale_log2;

@@ -80,8 +80,9 @@ fa_status fa_forward_f32(const float* q, const float* k, const float* v, float* 
                          int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                          hipStream_t stream);
 
-/* Bytes of device workspace fa_backward needs: one fp32 per query row (the
- * per-row term D_i = sum_t dO_it * O_it).  Returns 0 for invalid sizes. */
+/* Bytes of device workspace fa_backward needs: two fp32 per query row (the
+ * per-row term D_i = sum_t dO_it * O_it, and LSE_i in base-2 units).  Returns 0
+ * for invalid sizes. */
 size_t fa_backward_workspace_bytes(int B, int Hq, int N);
 
 /*
@@ -106,18 +107,23 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
  * can place them itself (after fa_backward_preprocess, fa_backward_dkdv and
  * fa_backward_dq only read the workspace and may run concurrently on two
  * streams).  Arguments, layouts and errors are those of fa_backward.
- *   fa_backward_preprocess: workspace[row] = D_row = sum_t dO_row,t * O_row,t (fp32).
- *   fa_backward_dkdv: dk, dv from q, k, v, dO, lse and the preprocessed workspace.
- *   fa_backward_dq:   dq from q, k, v, dO, lse and the preprocessed workspace.
+ *   fa_backward_preprocess: for every query row (b, h, i), row index
+ *     r = (b*Hq + h)*N + i, workspace as fp32 [2][B*Hq*N]:
+ *     workspace[r] = D_r = sum_t dO_r,t * O_r,t and
+ *     workspace[B*Hq*N + r] = lse[r] * log2(e).
+ *   fa_backward_dkdv: dk, dv from q, k, v, dO and the preprocessed workspace.
+ *   fa_backward_dq:   dq from q, k, v, dO and the preprocessed workspace.
+ * The last two read the saved statistic only through the workspace, so it must
+ * come from fa_backward_preprocess of the same o, dO and lse.
  */
-fa_status fa_backward_preprocess(const void* o, const void* dO, void* workspace, size_t workspace_bytes,
-                                 int B, int Hq, int N, int d, hipStream_t stream);
+fa_status fa_backward_preprocess(const void* o, const void* dO, const float* lse, void* workspace,
+                                 size_t workspace_bytes, int B, int Hq, int N, int d, hipStream_t stream);
 fa_status fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dO,
-                           const float* lse, const void* workspace, size_t workspace_bytes,
+                           const void* workspace, size_t workspace_bytes,
                            void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal,
                            float scale, hipStream_t stream);
 fa_status fa_backward_dq(const void* q, const void* k, const void* v, const void* dO,
-                         const float* lse, const void* workspace, size_t workspace_bytes,
+                         const void* workspace, size_t workspace_bytes,
                          void* dq, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                          hipStream_t stream);
 

@@ -41,7 +41,7 @@ def test_status_strings():
 
 def test_workspace_bytes():
     lib = api.load_library()
-    assert lib.fa_backward_workspace_bytes(2, 32, 8192) == 4 * 2 * 32 * 8192
+    assert lib.fa_backward_workspace_bytes(2, 32, 8192) == 2 * 4 * 2 * 32 * 8192
     assert lib.fa_backward_workspace_bytes(0, 1, 1) == 0
     assert lib.fa_backward_workspace_bytes(1, 1, -5) == 0
 
@@ -101,3 +101,21 @@ def test_backward_rejects_before_launch():
     bad[8] = base[7]  # dv aliases dk
     assert args(bad, ws, need) == 9
     assert args(base, base[0], need) == 9  # workspace aliases q
+
+
+def test_backward_steps_reject_before_launch():
+    lib = api.load_library()
+    dO, lse, ws, dq, dk, dv = (0x20_0000_0000, L, 0x60_0000_0000, 0x30_0000_0000, 0x40_0000_0000,
+                               0x50_0000_0000)
+    need = lib.fa_backward_workspace_bytes(1, 2, 16)
+    # preprocess reads o, dO and lse, writes the workspace (D and LSE in base 2)
+    assert lib.fa_backward_preprocess(O, dO, None, ws, need, 1, 2, 16, 64, None) == 1
+    assert lib.fa_backward_preprocess(O, dO, lse, ws, need - 4, 1, 2, 16, 64, None) == 8
+    assert lib.fa_backward_preprocess(O, dO, lse, lse, need, 1, 2, 16, 64, None) == 9
+    assert lib.fa_backward_preprocess(O, dO, lse, ws, need, 1, 2, 16, 48, None) == 4
+    # dK/dV and dQ read q, k, v, dO and the workspace only
+    assert lib.fa_backward_dkdv(Q, K, V, dO, None, need, dk, dv, 1, 2, 1, 16, 64, 1, 0.1, None) == 8
+    assert lib.fa_backward_dkdv(Q, K, V, dO, ws, need, dk, dk, 1, 2, 1, 16, 64, 1, 0.1, None) == 9
+    assert lib.fa_backward_dkdv(Q, K, V, dO, ws, need, dk, dv, 1, 2, 1, 16, 64, 2, 0.1, None) == 7
+    assert lib.fa_backward_dq(Q, K, V, dO, ws, need, Q, 1, 2, 1, 16, 64, 1, 0.1, None) == 9
+    assert lib.fa_backward_dq(Q, K, V, dO, ws, need, dq, 1, 3, 2, 16, 64, 1, 0.1, None) == 3
