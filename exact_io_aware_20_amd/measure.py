@@ -37,16 +37,18 @@ def fwd_bytes(B, Hq, Hkv, N, d, elt: int) -> int:
 
 
 def bwd_bytes(B, Hq, Hkv, N, d, elt: int) -> int:
-    """Read Q, O, dO, K, V, LSE; write dQ, dK, dV; D (fp32 per row) written and read."""
+    """Read Q, O, dO, K, V, LSE; write dQ, dK, dV; the two fp32 per-row terms (D and
+    LSE in base 2) written once and read by the dK/dV and dQ kernels."""
     q_sized = B * Hq * N * d
     kv_sized = B * Hkv * N * d
     return elt * (3 * q_sized + 2 * kv_sized) + 4 * B * Hq * N \
-        + elt * (q_sized + 2 * kv_sized) + 2 * 4 * B * Hq * N
+        + elt * (q_sized + 2 * kv_sized) + 3 * 2 * 4 * B * Hq * N
 
 
 def preprocess_bytes(B, Hq, N, d, elt: int) -> int:
-    """The backward preprocess reads O and dO and writes one fp32 D per row."""
-    return 2 * elt * B * Hq * N * d + 4 * B * Hq * N
+    """The backward preprocess reads O, dO and the fp32 LSE and writes two fp32 per row
+    (D and LSE in base 2)."""
+    return 2 * elt * B * Hq * N * d + 3 * 4 * B * Hq * N
 
 
 def score_matrix_bytes(N, elt: int = 4, heads: int = 1, batch: int = 1) -> int:

@@ -1,0 +1,178 @@
+"""Summaries of rocprofv3 output for the profiles/ folder, and the HBM traffic figure
+that bench.py reports beside its roofline.
+
+    python -m exact_io_aware_20_amd.profile_summary trace  <trace_dir> <out.md> <warmup_launches> <command>
+    python -m exact_io_aware_20_amd.profile_summary traffic <fetch_dir> <write_dir> <out.md> <calib_mib> <command>
+
+`trace` turns a `--kernel-trace --stats` run into a table of per-kernel launch
+counts and durations.  `traffic` reads two `--pmc` runs (FETCH_SIZE, then
+WRITE_SIZE, both in KiB per dispatch) of `bench.py --calib-copy-mib M`, which also
+launches one plain streaming kernel of known size (an elementwise negation of M MiB
+of fp32 into another M MiB buffer).  Each counter is scaled by the ratio of that
+kernel's true bytes to what the same counter reads for it, and the per-launch HBM
+bytes of every attention kernel are written with a digest of the kernel sources;
+bench.py uses the figure only while the sources still match the digest.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ("fa_fwd.hip", "fa_bwd.hip", "fa_common.hpp", "fa_launch.hpp")
+TRAFFIC_TAG = "traffic-json:"
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(kernel: str) -> str:
+    """'void fa::fa_bwd_dkdv_kernel<128>(fa::BwdParams)' -> 'fa_bwd_dkdv_kernel<128>'."""
+    k = kernel.split("(")[0]
+    k = re.sub(r"^void ", "", k)
+    return k.replace("fa::", "")
+
+
+def _find(pattern_dir: str, suffix: str) -> str:
+    hits = glob.glob(os.path.join(pattern_dir, "**", f"*{suffix}"), recursive=True)
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {pattern_dir}")
+    return sorted(hits)[0]
+
+
+def trace_table(trace_dir: str) -> list[dict]:
+    rows = []
+    with open(_find(trace_dir, "kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            rows.append({"kernel": short_name(r["Name"]), "calls": int(r["Calls"]),
+                         "avg_us": float(r["AverageNs"]) / 1e3, "min_us": float(r["MinNs"]) / 1e3,
+                         "max_us": float(r["MaxNs"]) / 1e3, "pct": float(r["Percentage"])})
+    return rows
+
+
+def timed_means(trace_dir: str, skip: int) -> dict[str, tuple[int, float]]:
+    """Per kernel: (launches kept, mean duration in us) over its dispatches in launch
+    order, leaving out the first `skip` of each (the untimed warm-up launches)."""
+    per = defaultdict(list)
+    with open(_find(trace_dir, "kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            per[short_name(r["Kernel_Name"])].append(
+                (int(r["Dispatch_Id"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    out = {}
+    for k, v in per.items():
+        kept = [d for _, d in sorted(v)[skip:]]
+        if kept:
+            out[k] = (len(kept), sum(kept) / len(kept))
+    return out
+
+
+def counter_means(pmc_dir: str, counter: str) -> dict[str, float]:
+    """Mean value of `counter` per dispatch for each kernel name."""
+    vals = defaultdict(list)
+    with open(_find(pmc_dir, "counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def calibration(means: dict[str, float]) -> tuple[str, float]:
+    hits = [(k, v) for k, v in means.items() if "neg_kernel" in k]
+    if len(hits) != 1:
+        raise RuntimeError("expected exactly one calibration (negation) kernel in the counter run")
+    return hits[0]
+
+
+def traffic(fetch_dir: str, write_dir: str, calib_mib: int) -> dict:
+    fetch = counter_means(fetch_dir, "FETCH_SIZE")
+    write = counter_means(write_dir, "WRITE_SIZE")
+    calib_bytes = calib_mib * 2**20
+    cname, cf = calibration(fetch)
+    _, cw = calibration(write)
+    f_scale = calib_bytes / (cf * 1024.0)
+    w_scale = calib_bytes / (cw * 1024.0)
+    out = {}
+    for k in fetch:
+        if "fa_" not in k:
+            continue
+        f_kib, w_kib = fetch[k], write.get(k, 0.0)
+        out[short_name(k)] = {"fetch_kib": f_kib, "write_kib": w_kib,
+                              "bytes": f_kib * 1024.0 * f_scale + w_kib * 1024.0 * w_scale}
+    return {"calib_kernel": short_name(cname), "calib_mib": calib_mib, "fetch_scale": f_scale,
+            "write_scale": w_scale, "kernels": out, "source_digest": source_digest()}
+
+
+def committed_traffic(md_path: str, kernel: str):
+    """HBM bytes per launch of `kernel` from a committed traffic summary, or None when
+    the file is missing or the kernel sources changed since the counters were taken."""
+    if not os.path.exists(md_path):
+        return None
+    with open(md_path) as f:
+        for line in f:
+            if line.startswith(TRAFFIC_TAG):
+                data = json.loads(line[len(TRAFFIC_TAG):])
+                if data.get("source_digest") != source_digest():
+                    return None
+                k = data["kernels"].get(kernel)
+                return None if k is None else k["bytes"]
+    return None
+
+
+def _write_trace_md(rows, timed, skip, out, command):
+    lines = [f"# Kernel trace: {os.path.splitext(os.path.basename(out))[0].replace('kernel_trace_', '')}", "",
+             "Command (from the repository root on the GPU box; `$R` is the repository path):", "",
+             f"    {command}", "",
+             f"Kernel sources digest: `{source_digest()}`.  `avg` is rocprofv3's own statistic over all "
+             f"launches; `timed avg` leaves out each kernel's first {skip} (warm-up) launches, the "
+             "figure comparable with bench.py's event timing of the timed steps.", "",
+             "| kernel | calls | avg (us) | min (us) | max (us) | share | timed avg (us) |",
+             "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        t = timed.get(r["kernel"])
+        ta = f"{t[1]:.1f} (n={t[0]})" if t else "-"
+        lines.append(f"| {r['kernel']} | {r['calls']} | {r['avg_us']:.1f} | {r['min_us']:.1f} | "
+                     f"{r['max_us']:.1f} | {r['pct']:.1f} % | {ta} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _write_traffic_md(t, out, command):
+    lines = [f"# HBM traffic per launch: {os.path.splitext(os.path.basename(out))[0].replace('hbm_traffic_', '')}", "",
+             "Two counter runs of the same command, one with `--pmc FETCH_SIZE`, one with",
+             "`--pmc WRITE_SIZE` (from the repository root on the GPU box; `$R` is the repository path):", "",
+             f"    {command}", "",
+             f"Calibration: `{t['calib_kernel']}` streams {t['calib_mib']} MiB in and {t['calib_mib']} MiB out; "
+             f"true bytes / counter bytes = {t['fetch_scale']:.3f} (FETCH_SIZE), {t['write_scale']:.3f} (WRITE_SIZE).",
+             "", "| kernel | FETCH_SIZE (KiB/dispatch) | WRITE_SIZE (KiB/dispatch) | calibrated HBM bytes / launch |",
+             "|---|---|---|---|"]
+    for k, v in sorted(t["kernels"].items()):
+        lines.append(f"| {k} | {v['fetch_kib']:.4g} | {v['write_kib']:.4g} | {v['bytes'] / 1e6:.1f} MB |")
+    lines += ["", f"Kernel sources digest: `{t['source_digest']}` (bench.py reports the figure only "
+              "while the sources match).", "", TRAFFIC_TAG + " " + json.dumps(t)]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def main(argv):
+    if len(argv) >= 5 and argv[0] == "trace":
+        skip = int(argv[3])
+        _write_trace_md(trace_table(argv[1]), timed_means(argv[1], skip), skip, argv[2], argv[4])
+    elif len(argv) >= 6 and argv[0] == "traffic":
+        _write_traffic_md(traffic(argv[1], argv[2], int(argv[4])), argv[3], argv[5])
+    else:
+        raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
