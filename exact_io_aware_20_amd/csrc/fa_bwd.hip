@@ -13,14 +13,14 @@
 // gfx950 mapping:
 //   * preprocess: per query row, D = dO . O and LSE in base-2 units, written to the
 //     workspace that the other two kernels read.
-//   * dK/dV kernel: a workgroup owns 128 keys of one KV head; waves 0-3 accumulate
-//     dK and waves 4-7 dV for 32 keys each (K, V in registers), streaming 64-row
-//     tiles of Q and dO of every query head in the group through LDS by direct
-//     loads.  S = Q K^T is formed with the query on the C rows, so P and dS feed
-//     the dV and dK contractions straight from registers; the Q^T and dO^T
-//     operands of those contractions come from the same natural tiles through the
-//     transposing LDS read.  The group sum over query heads happens in the
-//     accumulators (no atomics, bit-reproducible).
+//   * dK/dV kernel: a workgroup owns 128 keys of one KV head, 32 per pair of waves
+//     (one forms S, P and dV, its partner dP, dS and dK one item later, P handed
+//     over through LDS), streaming 64-row tiles of Q and dO of every query head in
+//     the group through LDS by direct loads.  S = Q K^T is formed with the query on
+//     the C rows, so P and dS feed the dV and dK contractions straight from
+//     registers; the Q^T and dO^T operands of those contractions come from the same
+//     natural tiles through the transposing LDS read.  The group sum over query
+//     heads happens in the accumulators (no atomics, bit-reproducible).
 //   * dQ kernel: a workgroup owns 32 query rows per wave of one query head (Q, dO,
 //     LSE, D in registers) and streams K/V tiles like the forward; S^T = K Q^T
 //     keeps each lane on one query, so LSE and D are lane-local, and the K^T
@@ -66,14 +66,16 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_pre_kernel(const uint16_t* o,
 // ---------------------------------------------------------------------------------
 template <int D>
 struct DkdvCfg {
-    static constexpr int WAVES = 8;          // 4 dK waves + 4 dV waves
+    static constexpr int WAVES = 8;          // 4 P/dV waves + 4 dS/dK waves
     static constexpr int THREADS = WAVES * kWave;
     static constexpr int BK = 4 * 32;        // keys per workgroup
     static constexpr int BQ = 64;            // query rows per streamed tile
     static constexpr int DC = D / 16;
     static constexpr int DB = D / 32;
-    static constexpr int NAT = SwzTile<D, 1>::ELEMS;   // natural Q or dO tile (bf16 elements)
+    static constexpr int NAT = SwzTile<D, 1>::ELEMS;    // natural Q or dO tile (bf16 elements)
     static constexpr int STAGE = 2 * NAT + 2 * BQ * 2;  // Q, dO, then LSE2 and D (fp32, BQ each)
+    static constexpr int NSTAGE = 3;                    // items it+1 (loading), it, it-1
+    static constexpr int PBUF = 4 * 32 * 64 * 2;        // fp32 P of one item: 4 pairs x 32 x 64 lanes (bf16 units)
 };
 
 // C[q][key] = sum_d A[q][d] B[key][d] for query half qb (32 rows) of a natural
@@ -97,29 +99,21 @@ __device__ __forceinline__ void mask_half(f32x16& s, int qrow0, int key, int N, 
     }
 }
 
-// One query half: P = 2^(S*sl2 - LSE2); dK waves form dS = P (dP - D) and
-// accumulate dK^T += Q^T dS, dV waves accumulate dV^T += dO^T P, the A operand
-// (`tt`: Q or dO tile) read transposed.  Register 4g+i of a C tile is k-slot
-// 4(g%2)+i of fragment g/2 (query 8g + 4hh + i of the half).
-template <int D, bool DK>
-__device__ __forceinline__ void grads_half(const f32x16& s, const f32x16& dp, const uint16_t* tt, const float* lse2,
-                                           const float* dvec, f32x16 (&acc)[D / 32], float sl2, int qb, int lane,
-                                           int hh) {
-    u32x4 bf[2];
+// Register 4g+i of a C tile (query 8g + 4hh + i of its half) packed as k-slot
+// 4(g%2)+i of B fragment g/2 (two fragments of 16 queries per half).
+__device__ __forceinline__ void pack_half(const f32x16& x, u32x4 (&bf)[2]) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        const f32x4 L = *(const f32x4*)(lse2 + 32 * qb + 8 * g + 4 * hh);
-        float pv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(__builtin_fmaf(s[4 * g + i], sl2, -L[i]));
-        if (DK) {
-            const f32x4 Dd = *(const f32x4*)(dvec + 32 * qb + 8 * g + 4 * hh);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pv[i] *= dp[4 * g + i] - Dd[i];
-        }
-        bf[g >> 1][2 * (g & 1)] = pack_bf16(pv[0], pv[1]);
-        bf[g >> 1][2 * (g & 1) + 1] = pack_bf16(pv[2], pv[3]);
+        bf[g >> 1][2 * (g & 1)] = pack_bf16(x[4 * g], x[4 * g + 1]);
+        bf[g >> 1][2 * (g & 1) + 1] = pack_bf16(x[4 * g + 2], x[4 * g + 3]);
     }
+}
+
+// acc^T += T^T X over one query half: A operand read transposed from the natural
+// tile `tt` (Q or dO), B operand the packed half `bf`.
+template <int D>
+__device__ __forceinline__ void acc_half(const uint16_t* tt, const u32x4 (&bf)[2], f32x16 (&acc)[D / 32], int qb,
+                                         int lane) {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -127,15 +121,22 @@ __device__ __forceinline__ void grads_half(const f32x16& s, const f32x16& dp, co
             acc[db] = mfma32x32x16(tr_frag<D>(tt, db, 32 * qb + 16 * h2, lane), bf[h2], acc[db]);
 }
 
-// dK/dV kernel.  A workgroup owns 128 keys of one KV head; waves 0-3 accumulate
-// dK and waves 4-7 dV for keys 32(w%4) .. +31, so each wave holds one accumulator
-// set and two waves fit per SIMD.  Both recompute S; the dK wave also forms dP.
-// Items are (query head of the group, 64-row query tile); item it's Q and dO tiles
-// and its LSE2/D vectors sit in stage it&1 of LDS, all filled by direct loads.
-// Iteration it: wait for item it's loads and a workgroup barrier (so stage
-// (it+1)&1, last used by item it-1, is free), issue item it+1's loads into it,
-// then compute item it.
-template <int D, bool DK>
+// dK/dV kernel.  A workgroup owns 128 keys of one KV head.  Wave w < 4 ("P/dV")
+// and wave w + 4 ("dS/dK") own keys 32w .. 32w+31; the first computes S = Q K^T,
+// P = 2^(S*sl2 - LSE2) and dV^T += dO^T P for item it and hands P (fp32) to its
+// partner through LDS; the partner, one item behind, computes dP = dO V^T,
+// dS = P (dP - D) and dK^T += Q^T dS for item it-1.  S and the exponentials are
+// thus formed once per item.  Items are (query head of the group, 64-row query
+// tile); their Q and dO tiles and LSE2/D vectors sit in stage it%3 of LDS, filled
+// by direct loads.  Iteration it:
+//   barrier A: item it landed; items it-1 (still read by dS/dK) and it stay, the
+//              stage of item it-2 is free and receives item it+1's loads;
+//   P/dV: S, mask, P of item it;        dS/dK: P(it-1) from LDS, dP of item it-1;
+//   barrier B (P(it-1) has been read);
+//   P/dV: P(it) to LDS, dV MFMAs;       dS/dK: dS and dK MFMAs of item it-1.
+// In each half one wave of a SIMD pair runs exponentials or dS while the other
+// runs matrix work.
+template <int D, bool PV>
 __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, int wave, int lane) {
     using C = DkdvCfg<D>;
     const int l32 = lane & 31;
@@ -153,13 +154,11 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, in
     const int key = kw0 + l32;
 
     const size_t kvoff = (size_t)head_kv * N * D;
-    // K (both roles) and V (dK waves) as B operands (lane: key, slots: 8 d)
-    u32x4 kf[C::DC], vf[DK ? C::DC : 1];
+    // K (P/dV waves) or V (dS/dK waves) as B operands (lane: key, slots: 8 d)
+    const uint16_t* kv = (const uint16_t*)(PV ? p.k : p.v) + kvoff;
+    u32x4 bfr[C::DC];
 #pragma unroll
-    for (int c = 0; c < C::DC; ++c) {
-        kf[c] = key < N ? ld_global16((const uint16_t*)p.k + kvoff + (size_t)key * D + 16 * c + 8 * hh) : zero_u4();
-        if constexpr (DK) vf[c] = key < N ? ld_global16((const uint16_t*)p.v + kvoff + (size_t)key * D + 16 * c + 8 * hh) : zero_u4();
-    }
+    for (int c = 0; c < C::DC; ++c) bfr[c] = key < N ? ld_global16(kv + (size_t)key * D + 16 * c + 8 * hh) : zero_u4();
     f32x16 acc[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) acc[db] = zero16();
@@ -169,14 +168,16 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, in
     const int per_head = nqt - qt_start;
     const int nitems = G * per_head;
     const float sl2 = p.scale_log2;
+    float* pbuf = (float*)(smem + C::NSTAGE * C::STAGE) + (wave & 3) * 32 * 64;   // this pair's P slots
 
     TileDma<D, 1, C::WAVES> dma;
     dma.init(wave, lane);
+    auto item_q0 = [&](int it) { return (qt_start + it % per_head) * C::BQ; };
     auto issue_item = [&](int it) {
         const int hq = hkv * G + it / per_head;
-        const int q0 = (qt_start + it % per_head) * C::BQ;
+        const int q0 = item_q0(it);
         const size_t roff = (size_t)(b * p.Hq + hq) * N + q0;
-        uint16_t* st = smem + (it & 1) * C::STAGE;
+        uint16_t* st = smem + (it % C::NSTAGE) * C::STAGE;
         dma.issue((const uint16_t*)p.q + roff * D, N - q0, st, wave);
         dma.issue((const uint16_t*)p.dO + roff * D, N - q0, st + C::NAT, wave);
         // LSE2 (wave 0) and D (wave 1): 4 bytes per lane; rows >= N read row N-1
@@ -185,32 +186,86 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, in
             __builtin_amdgcn_global_load_lds(src, (lds_void*)(st + 2 * C::NAT + wave * 2 * C::BQ), 4, 0, 0);
         }
     };
+    // keys of this wave visible to some row of the item's tile
+    auto active = [&](int q0) { return kw0 < N && (!p.causal || q0 + C::BQ - 1 >= kw0); };
 
     if (nitems > 0) issue_item(0);
-    for (int it = 0; it < nitems; ++it) {
-        const int q0 = (qt_start + it % per_head) * C::BQ;
-        const uint16_t* st = smem + (it & 1) * C::STAGE;
+    for (int it = 0; it <= nitems; ++it) {
+        const int mine = PV ? it : it - 1;            // item this wave works on
+        const bool have = PV ? it < nitems : it >= 1;
+        const int q0 = have ? item_q0(mine) : 0;
+        const uint16_t* st = smem + ((mine + C::NSTAGE) % C::NSTAGE) * C::STAGE;
         const float* lse2 = (const float*)(st + 2 * C::NAT);
         const float* dvec = lse2 + C::BQ;
+        const bool act = have && active(q0);
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        __syncthreads();                                               // A
         if (it + 1 < nitems) issue_item(it + 1);
-        const bool act = kw0 < N && (!p.causal || q0 + C::BQ - 1 >= kw0);
-        const bool mask = (p.causal && q0 < kw0 + 31) || (q0 + C::BQ > N);
+        f32x16 x[2];                                                   // P (P/dV) or dP (dS/dK)
+        f32x16 pp[2];                                                  // dS/dK: P of its item
         if (act) {
+            if constexpr (PV) {
+                const bool mask = (p.causal && q0 < kw0 + 31) || (q0 + C::BQ > N);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                f32x16 s = qk_half<D>(st, kf, qb, l32, hh), dp = zero16();
-                if constexpr (DK) dp = qk_half<D>(st + C::NAT, vf, qb, l32, hh);
-                if (mask) mask_half(s, q0 + 32 * qb + 4 * hh, key, N, p.causal);
-                grads_half<D, DK>(s, dp, st + (DK ? 0 : C::NAT), lse2, dvec, acc, sl2, qb, lane, hh);
+                for (int qb = 0; qb < 2; ++qb) {
+                    x[qb] = qk_half<D>(st, bfr, qb, l32, hh);
+                    if (mask) mask_half(x[qb], q0 + 32 * qb + 4 * hh, key, N, p.causal);
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 L = *(const f32x4*)(lse2 + 32 * qb + 8 * g + 4 * hh);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            x[qb][4 * g + i] = fast_exp2(__builtin_fmaf(x[qb][4 * g + i], sl2, -L[i]));
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 v = *(const f32x4*)(pbuf + (4 * qb + g) * 4 * 64 + 4 * lane);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) pp[qb][4 * g + i] = v[i];
+                    }
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) x[qb] = qk_half<D>(st + C::NAT, bfr, qb, l32, hh);
+            }
+        }
+        __syncthreads();                                               // B
+        if (act) {
+            if constexpr (PV) {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *(f32x4*)(pbuf + (4 * qb + g) * 4 * 64 + 4 * lane) =
+                            f32x4{x[qb][4 * g], x[qb][4 * g + 1], x[qb][4 * g + 2], x[qb][4 * g + 3]};
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    u32x4 bf[2];
+                    pack_half(x[qb], bf);
+                    acc_half<D>(st + C::NAT, bf, acc, qb, lane);       // dV^T += dO^T P
+                }
+            } else {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 Dd = *(const f32x4*)(dvec + 32 * qb + 8 * g + 4 * hh);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) x[qb][4 * g + i] = pp[qb][4 * g + i] * (x[qb][4 * g + i] - Dd[i]);
+                    }
+                    u32x4 bf[2];
+                    pack_half(x[qb], bf);
+                    acc_half<D>(st, bf, acc, qb, lane);                // dK^T += Q^T dS
+                }
             }
         }
     }
 
     if (key < N) {
-        uint16_t* dst = (uint16_t*)(DK ? p.dk : p.dv) + kvoff + (size_t)key * D;
-        const float sc = DK ? p.scale : 1.f;
+        uint16_t* dst = (uint16_t*)(PV ? p.dv : p.dk) + kvoff + (size_t)key * D;
+        const float sc = PV ? 1.f : p.scale;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -224,10 +279,11 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, in
 template <int D>
 __global__ __launch_bounds__(DkdvCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * DkdvCfg<D>::STAGE];
+    using C = DkdvCfg<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[C::NSTAGE * C::STAGE + C::PBUF];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    __builtin_assume(wave < DkdvCfg<D>::WAVES);
+    __builtin_assume(wave < C::WAVES);
     if (wave < 4)
         dkdv_role<D, true>(p, smem, wave, tid & 63);
     else
