@@ -261,3 +261,42 @@ def test_long_context_sampled_rows(causal):
         assert_o_bf16(o_h[b, h, rows], o_ref[b, h, rows], f"head {h}")
         assert np.abs(lse_h[b, h, rows] - lse_ref[b, h, rows]).max() <= 1e-2
         assert np.abs(lse_ref[b, h, rows]).max() > 100   # the logits really are large
+
+
+def test_backward_steps_match_fused_call():
+    # the three entry points fa_backward enqueues, called one by one (dK/dV and dQ on
+    # two streams after the preprocess), give bit-identical gradients
+    B, Hq, Hkv, N, d = 1, 4, 2, 300, 128
+    host, g = make(B, Hq, Hkv, N, d, seed=9950, with_do=True)
+    o, lse = api.forward(g["q"], g["k"], g["v"], True, 0.09)
+    dq, dk, dv = api.backward(g["q"], g["k"], g["v"], o, g["do"], lse, True, 0.09)
+    dq2, dk2, dv2 = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+    ws = torch.empty(api.workspace_bytes(B, Hq, N), dtype=torch.uint8, device=dev())
+    api.backward_steps(g["q"], g["k"], g["v"], o, g["do"], lse, True, 0.09, dq2, dk2, dv2, ws, steps=("pre",))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    api.backward_steps(g["q"], g["k"], g["v"], o, g["do"], lse, True, 0.09, dq2, dk2, dv2, ws, stream=s1,
+                       steps=("dkdv",))
+    api.backward_steps(g["q"], g["k"], g["v"], o, g["do"], lse, True, 0.09, dq2, dk2, dv2, ws, stream=s2,
+                       steps=("dq",))
+    torch.cuda.synchronize()
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_preprocess_workspace_contents():
+    # workspace = [D_r = dO_r . O_r | LSE_r * log2(e)], fp32, r = (b*Hq + h)*N + i
+    B, Hq, N, d = 2, 3, 77, 64
+    host, g = make(B, Hq, Hq, N, d, seed=9960, with_do=True)
+    o, lse = api.forward(g["q"], g["k"], g["v"], False, 0.125)
+    ws = torch.zeros(api.workspace_bytes(B, Hq, N), dtype=torch.uint8, device=dev())
+    dq, dk, dv = torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"])
+    api.backward_steps(g["q"], g["k"], g["v"], o, g["do"], lse, False, 0.125, dq, dk, dv, ws, steps=("pre",))
+    torch.cuda.synchronize()
+    w = ws.view(torch.float32).cpu().numpy()
+    rows = B * Hq * N
+    d_ref = (f64(g["do"]) * f64(o)).sum(axis=-1).reshape(-1)
+    assert np.abs(w[:rows] - d_ref).max() <= 1e-5 * max(1.0, np.abs(d_ref).max())
+    lse2 = (lse.cpu().reshape(-1) * torch.tensor(1.4426950408889634, dtype=torch.float32)).numpy()
+    assert np.array_equal(w[rows:2 * rows], lse2)
