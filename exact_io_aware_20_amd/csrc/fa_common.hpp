@@ -154,30 +154,44 @@ __device__ __forceinline__ int swz_tile_issue(const uint16_t* src, int nvalid, u
 }
 
 // The same loads with the per-lane source offsets computed once: a wave's chunk
-// positions in the tile do not change from tile to tile, so issuing a tile costs
-// a clamp and an address add per load.  `wave` must be below NWAVES.
+// positions in the tile do not change from tile to tile, so a full tile costs one
+// load per chunk from a uniform base plus a 32-bit lane offset; only a ragged last
+// tile (wave-uniform branch) clamps its rows.  `wave` must be below NWAVES.
 template <int D, int MODE, int NWAVES>
 struct TileDma {
     using S = SwzTile<D, MODE>;
     static constexpr int PER = (S::WAVE_LOADS + NWAVES - 1) / NWAVES;
-    int off[PER];   // element offset of this lane's 16-byte chunk within the global tile
-    int row[PER];   // its tile row
+    uint32_t off[PER];   // byte offset of this lane's 16-byte chunk within the global tile
     __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
-            const int pos = (wave + k * NWAVES) * 64 + lane;
-            row[k] = pos / S::CHUNKS;
-            off[k] = row[k] * D + ((pos % S::CHUNKS) ^ S::swz(row[k])) * 8;
+            const uint32_t pos = (uint32_t)((wave + k * NWAVES) * 64 + lane);
+            const uint32_t row = pos / S::CHUNKS;
+            off[k] = (row * D + ((pos % S::CHUNKS) ^ (uint32_t)S::swz((int)row)) * 8) * 2;
         }
     }
     // rows at or past `nvalid` are read from row nvalid-1 (in bounds, never used)
     __device__ __forceinline__ void issue(const uint16_t* src, int nvalid, uint16_t* lds_tile, int wave) const {
+        const char* base = (const char*)src;
+        if (nvalid >= 64) {
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int i = wave + k * NWAVES;
-            if (S::WAVE_LOADS % NWAVES == 0 || i < S::WAVE_LOADS) {
-                const int o = off[k] + (min(row[k], nvalid - 1) - row[k]) * D;
-                __builtin_amdgcn_global_load_lds(src + o, (lds_void*)(lds_tile + i * 64 * 8), 16, 0, 0);
+            for (int k = 0; k < PER; ++k) {
+                const int i = wave + k * NWAVES;
+                if (S::WAVE_LOADS % NWAVES == 0 || i < S::WAVE_LOADS)
+                    __builtin_amdgcn_global_load_lds((const uint16_t*)(base + off[k]),
+                                                     (lds_void*)(lds_tile + i * 64 * 8), 16, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int i = wave + k * NWAVES;
+                if (S::WAVE_LOADS % NWAVES == 0 || i < S::WAVE_LOADS) {
+                    const uint32_t row = off[k] / (2 * D);
+                    const uint32_t last = (uint32_t)(nvalid - 1);
+                    const uint32_t rr = row < last ? row : last;
+                    __builtin_amdgcn_global_load_lds((const uint16_t*)(base + (off[k] - (row - rr) * (2 * D))),
+                                                     (lds_void*)(lds_tile + i * 64 * 8), 16, 0, 0);
+                }
             }
         }
     }

@@ -98,7 +98,7 @@ __device__ __forceinline__ void fwd_rescale(const f32x16 (&s)[2], f32x16 (&o)[D 
     mx = pair_max(mx);
     const float mt = mx * sl2;   // sl2 > 0, so -inf stays -inf
     const bool need = mt > m_ref + kRescaleLog2;
-    if (__ballot(need)) {
+    if (__builtin_expect(__ballot(need) != 0, 0)) {
         const float mnew = need ? mt : m_ref;
         const float alpha = m_ref == kNegInf ? 0.f : fast_exp2(m_ref - mnew);
         m_ref = mnew;
@@ -198,12 +198,12 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     float m_ref = kNegInf, l_part = 0.f;
     const float sl2 = p.scale_log2;
 
-    auto issue_k = [&](int t, uint16_t* buf) {
-        swz_tile_issue<D, 0, C::WAVES>(Kh + (size_t)t * C::BC * D, N - t * C::BC, buf, wave, lane);
-    };
-    auto issue_v = [&](int t, uint16_t* buf) {
-        swz_tile_issue<D, 1, C::WAVES>(Vh + (size_t)t * C::BC * D, N - t * C::BC, buf, wave, lane);
-    };
+    TileDma<D, 0, C::WAVES> kdma;
+    TileDma<D, 1, C::WAVES> vdma;
+    kdma.init(wave, lane);
+    vdma.init(wave, lane);
+    auto issue_k = [&](int t, uint16_t* buf) { kdma.issue(Kh + (size_t)t * C::BC * D, N - t * C::BC, buf, wave); };
+    auto issue_v = [&](int t, uint16_t* buf) { vdma.issue(Vh + (size_t)t * C::BC * D, N - t * C::BC, buf, wave); };
 
     // prologue: K(0), V(0) -> LDS; S(0); K(1) -> LDS
     issue_k(0, kbuf);
