@@ -118,45 +118,12 @@ struct SwzTile {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Returns x unchanged, but opaque to the optimiser: per-lane address arithmetic
-// that depends on it is recomputed where it is used instead of being hoisted out
-// of the main loop and kept live (which would spill under full register use).
-__device__ __forceinline__ int opaque(int x) {
-    asm volatile("" : "+v"(x));
-    return x;
-}
-
-// Issue the direct loads of one 64-row tile: wave-instruction i (of WAVE_LOADS)
-// covers LDS chunk positions [64 i, 64 i + 64).  Rows at or past `nvalid` are
-// read from row nvalid-1 instead (always in bounds; callers mask those rows or
-// give them zero weight).
-template <int D, int MODE, int NWAVES>
-__device__ __forceinline__ int swz_tile_issue(const uint16_t* src, int nvalid, uint16_t* lds_tile,
-                                              int wave, int lane) {
-    using S = SwzTile<D, MODE>;
-    lane = opaque(lane);
-    int issued = 0;
-#pragma unroll
-    for (int k = 0; k < (S::WAVE_LOADS + NWAVES - 1) / NWAVES; ++k) {
-        const int i = wave + k * NWAVES;
-        if (i < S::WAVE_LOADS) {
-            const int pos = i * 64 + lane;
-            const int r = pos / S::CHUNKS;
-            const int slot = pos % S::CHUNKS;
-            const int j = slot ^ S::swz(r);
-            const int rr = r < nvalid ? r : nvalid - 1;
-            __builtin_amdgcn_global_load_lds(src + (size_t)rr * D + j * 8,
-                                             (lds_void*)(lds_tile + i * 64 * 8), 16, 0, 0);
-            ++issued;
-        }
-    }
-    return issued;
-}
-
-// The same loads with the per-lane source offsets computed once: a wave's chunk
-// positions in the tile do not change from tile to tile, so a full tile costs one
-// load per chunk from a uniform base plus a 32-bit lane offset; only a ragged last
-// tile (wave-uniform branch) clamps its rows.  `wave` must be below NWAVES.
+// Direct loads of one 64-row tile: wave-instruction i (of WAVE_LOADS, spread over
+// NWAVES waves) covers LDS chunk positions [64 i, 64 i + 64).  A wave's chunk
+// positions do not change from tile to tile, so the per-lane source offsets are
+// computed once and a full tile costs one load per chunk from a uniform base plus
+// a 32-bit lane offset; only a ragged last tile (wave-uniform branch) clamps its
+// rows.  `wave` must be below NWAVES.
 template <int D, int MODE, int NWAVES>
 struct TileDma {
     using S = SwzTile<D, MODE>;
