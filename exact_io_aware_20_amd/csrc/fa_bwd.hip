@@ -203,6 +203,8 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, in
         if (it + 1 < nitems) issue_item(it + 1);
         f32x16 x[2];                                                   // P (P/dV) or dP (dS/dK)
         f32x16 pp[2];                                                  // dS/dK: P of its item
+        // each half's critical wave (P/dV before barrier B, dS/dK after) issues first
+        __builtin_amdgcn_s_setprio(PV ? 2 : 0);
         if (act) {
             if constexpr (PV) {
                 const bool mask = (p.causal && q0 < kw0 + 31) || (q0 + C::BQ > N);
@@ -232,6 +234,7 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, in
             }
         }
         __syncthreads();                                               // B
+        __builtin_amdgcn_s_setprio(PV ? 0 : 2);
         if (act) {
             if constexpr (PV) {
 #pragma unroll
@@ -263,6 +266,7 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, in
         }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     if (key < N) {
         uint16_t* dst = (uint16_t*)(PV ? p.dv : p.dk) + kvoff + (size_t)key * D;
         const float sc = PV ? 1.f : p.scale;
