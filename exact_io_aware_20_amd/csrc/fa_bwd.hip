@@ -146,7 +146,7 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, in
 
     const int ntile_k = (N + C::BK - 1) / C::BK;
     int head_kv, kt;
-    map_block(blockIdx.x, gridDim.x, ntile_k, p.B * p.Hkv, false, head_kv, kt);
+    map_block(blockIdx.x, gridDim.x, ntile_k, p.B * p.Hkv, false, head_kv, kt, 4);
     const int b = head_kv / p.Hkv;
     const int hkv = head_kv % p.Hkv;
     const int k0 = kt * C::BK;
@@ -331,7 +331,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
 
     const int ntile_q = (N + C::BR - 1) / C::BR;
     int head, qt;
-    map_block(blockIdx.x, gridDim.x, ntile_q, p.B * p.Hq, p.causal != 0, head, qt);
+    map_block(blockIdx.x, gridDim.x, ntile_q, p.B * p.Hq, p.causal != 0, head, qt, 4);
     const int hq = head % p.Hq;
     const int b = head / p.Hq;
     const int hkv = hq / (p.Hq / p.Hkv);

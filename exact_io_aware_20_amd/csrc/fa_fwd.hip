@@ -169,7 +169,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 
     const int ntile_q = (N + C::BR - 1) / C::BR;
     int head, qt;
-    map_block(blockIdx.x, gridDim.x, ntile_q, p.B * p.Hq, p.causal != 0, head, qt);
+    map_block(blockIdx.x, gridDim.x, ntile_q, p.B * p.Hq, p.causal != 0, head, qt, 4);
     const int hq = head % p.Hq;
     const int b = head / p.Hq;
     const int hkv = hq / (p.Hq / p.Hkv);

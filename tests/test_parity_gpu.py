@@ -228,6 +228,9 @@ def test_full_size_workload(name):
     o_ref, lse_ref = oracle.attention_forward(host["q"], host["k"], host["v"], True, w.scale,
                                               heads=heads, workers=WORKERS)
     o_h, lse_h = f64(o), f64(lse)
+    o_err = max(np.abs(o_h[b, h] - o_ref[b, h]).max() for b, h in heads)
+    lse_err = max(np.abs(lse_h[b, h] - lse_ref[b, h]).max() for b, h in heads)
+    print(f"\n[parity] {name}: {len(heads)} heads, O max-abs {o_err:.3g}, LSE max-abs {lse_err:.3g}")
     for b, h in heads:
         assert_o_bf16(o_h[b, h], o_ref[b, h], f"{name} head {(b, h)}")
         assert np.abs(lse_h[b, h] - lse_ref[b, h]).max() <= 1e-2
@@ -235,11 +238,14 @@ def test_full_size_workload(name):
         dq_r, dk_r, dv_r = oracle.attention_backward(host["q"], host["k"], host["v"], host["do"], True,
                                                      w.scale, groups=groups, workers=WORKERS)
         dq_h, dk_h, dv_h = f64(dq), f64(dk), f64(dv)
+        e = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
         for b, hk in groups:
-            assert rel_l2(dk_h[b, hk], dk_r[b, hk]) <= 1e-2
-            assert rel_l2(dv_h[b, hk], dv_r[b, hk]) <= 1e-2
+            e["dk"] = max(e["dk"], rel_l2(dk_h[b, hk], dk_r[b, hk]))
+            e["dv"] = max(e["dv"], rel_l2(dv_h[b, hk], dv_r[b, hk]))
             for h in range(hk * G, hk * G + G):
-                assert rel_l2(dq_h[b, h], dq_r[b, h]) <= 1e-2
+                e["dq"] = max(e["dq"], rel_l2(dq_h[b, h], dq_r[b, h]))
+        print(f"[parity] {name}: {len(groups)} KV groups, rel-L2 dQ {e['dq']:.3g} dK {e['dk']:.3g} dV {e['dv']:.3g}")
+        assert max(e.values()) <= 1e-2
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -257,6 +263,10 @@ def test_long_context_sampled_rows(causal):
     o_ref, lse_ref = oracle.attention_forward(host["q"], host["k"], host["v"], causal, w.scale,
                                               heads=heads, rows=rows, workers=WORKERS)
     o_h, lse_h = f64(o), f64(lse)
+    o_err = max(np.abs(o_h[b, h, rows] - o_ref[b, h, rows]).max() for b, h in heads)
+    lse_err = max(np.abs(lse_h[b, h, rows] - lse_ref[b, h, rows]).max() for b, h in heads)
+    print(f"\n[parity] longctx causal={causal}: {len(heads)} heads x {len(rows)} rows, "
+          f"O max-abs {o_err:.3g}, LSE max-abs {lse_err:.3g}")
     for b, h in heads:
         assert_o_bf16(o_h[b, h, rows], o_ref[b, h, rows], f"head {h}")
         assert np.abs(lse_h[b, h, rows] - lse_ref[b, h, rows]).max() <= 1e-2
@@ -300,3 +310,17 @@ def test_preprocess_workspace_contents():
     assert np.abs(w[:rows] - d_ref).max() <= 1e-5 * max(1.0, np.abs(d_ref).max())
     lse2 = (lse.cpu().reshape(-1) * torch.tensor(1.4426950408889634, dtype=torch.float32)).numpy()
     assert np.array_equal(w[rows:2 * rows], lse2)
+
+
+def test_tiny_f32_workload():
+    # the all-fp32 configuration with its own seeded inputs, against the fp64 oracle
+    w = inputs.WORKLOADS["tiny_f32"]
+    host = inputs.workload_inputs(w)
+    g = {k: v.to(dev()) for k, v in host.items()}
+    for causal in w.causal:
+        o, lse = api.forward_f32(g["q"], g["k"], g["v"], causal, w.scale)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.attention_forward(host["q"], host["k"], host["v"], causal, w.scale)
+        o_err, lse_err = np.abs(f64(o) - o_ref).max(), np.abs(f64(lse) - lse_ref).max()
+        print(f"\n[parity] tiny_f32 causal={causal}: O max-abs {o_err:.3g}, LSE max-abs {lse_err:.3g}")
+        assert o_err <= 1e-5 and lse_err <= 1e-5
