@@ -3,9 +3,9 @@
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, the package's smoke check and the
 benchmark's CPU-baseline leg, never by the HIP library or its binding.
 """
-from .attention import (attention_backward, attention_forward, head_backward,
-                        head_forward, head_probs)
+from .attention import (attention_backward, attention_forward, decode_forward,
+                        head_backward, head_forward, head_probs)
 from .online import head_forward_tiled, online_softmax_states
 
-__all__ = ["attention_forward", "attention_backward", "head_forward", "head_backward",
+__all__ = ["attention_forward", "attention_backward", "decode_forward", "head_forward", "head_backward",
            "head_probs", "head_forward_tiled", "online_softmax_states"]

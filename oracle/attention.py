@@ -30,6 +30,12 @@ Readings where the pages are silent (each listed with its reason in the design n
 * The scale is the caller's (configs pass 1/sqrt(d)).
 * The saved statistic is the natural-log log-sum-exp of the *scaled* logits.
 * Query head hq uses KV head hq // (Hq / Hkv) (contiguous groups).
+* Decoding against a key/value cache (``decode_forward``): the Nq queries are the
+  last Nq tokens of a sequence whose Nk keys and values, their own included, are all
+  in the cache (lecture summary, section "衡量并优化推理": decoding reuses the keys
+  and values of earlier tokens instead of recomputing them).  Query i therefore sits
+  at position Nk - Nq + i, and causally sees keys j <= Nk - Nq + i; with Nq = Nk
+  this is the ordinary causal mask.
 * The gradients are the analytic softmax-Jacobian gradients (the pages print none):
       dP = dO V^T,  D_i = sum_j P_ij dP_ij,  dS = P * (dP - D),
       dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO,
@@ -62,7 +68,9 @@ def _f64(x) -> np.ndarray:
 
 
 def _scores(q_rows: np.ndarray, k: np.ndarray, rows: np.ndarray, causal: bool, scale: float):
-    """S for the given query rows against all keys, with the causal mask applied."""
+    """S for the given query rows against all keys, with the causal mask applied.
+
+    ``rows`` are the queries' positions in the key sequence."""
     s = scale * (q_rows @ k.T)
     if causal:
         cols = np.arange(k.shape[0])
@@ -70,13 +78,19 @@ def _scores(q_rows: np.ndarray, k: np.ndarray, rows: np.ndarray, causal: bool, s
     return s
 
 
-def head_forward(q, k, v, causal: bool, scale: float, rows=None):
+def _query_offset(nq: int, nk: int) -> int:
+    """Position of query row 0 in the key sequence: the queries are its last nq tokens."""
+    return nk - nq
+
+
+def head_forward(q, k, v, causal: bool, scale: float, rows=None, offset: int = 0):
     """One query head: O and LSE for the selected query rows (default: all rows).
 
-    q: [N, d]; k, v: [N, d] (the KV head of this query's group).  Returns
-    (O [len(rows), d], LSE [len(rows)]) in float64.  A row with no visible key
-    (not reachable when queries and keys have the same length) gives O = 0 and
-    LSE = -inf.
+    q: [Nq, d]; k, v: [Nk, d] (the KV head of this query's group); query row i sits
+    at position i + offset of the key sequence (offset 0 when queries and keys are
+    the same sequence).  Returns (O [len(rows), d], LSE [len(rows)]) in float64.  A
+    row with no visible key (not reachable when the queries are the tail of the key
+    sequence) gives O = 0 and LSE = -inf.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     n = q.shape[0]
@@ -85,7 +99,7 @@ def head_forward(q, k, v, causal: bool, scale: float, rows=None):
     lse = np.full(rows.size, -np.inf)
     for b0 in range(0, rows.size, ROW_BLOCK):
         r = rows[b0:b0 + ROW_BLOCK]
-        s = _scores(q[r], k, r, causal, scale)
+        s = _scores(q[r], k, r + offset, causal, scale)
         m = s.max(axis=1)                              # pass 1: row max
         ok = np.isfinite(m)
         e = np.exp(s - np.where(ok, m, 0.0)[:, None])  # pass 2: exponentials
@@ -150,8 +164,8 @@ def _check_shapes(q, k, v):
 
 
 def _fwd_unit(args):
-    q, k, v, causal, scale, rows = args
-    return head_forward(q, k, v, causal, scale, rows)
+    q, k, v, causal, scale, rows, offset = args
+    return head_forward(q, k, v, causal, scale, rows, offset)
 
 
 def _bwd_unit(args):
@@ -198,7 +212,7 @@ def attention_forward(q, k, v, causal: bool, scale: float, heads=None, rows=None
     heads = [(b, h) for b in range(b_) for h in range(hq_)] if heads is None else list(heads)
     o = np.full(q.shape, np.nan)
     lse = np.full(q.shape[:3], np.nan)
-    jobs = [(q[b, h], k[b, _group(h, hq_, hkv_)], v[b, _group(h, hq_, hkv_)], causal, scale, rows)
+    jobs = [(q[b, h], k[b, _group(h, hq_, hkv_)], v[b, _group(h, hq_, hkv_)], causal, scale, rows, 0)
             for b, h in heads]
     results = _run(_fwd_unit, jobs, workers)
     sel = slice(None) if rows is None else np.asarray(rows)
@@ -234,3 +248,30 @@ def attention_backward(q, k, v, do, causal: bool, scale: float, groups=None, wor
         dk[b, hk] += dkh
         dv[b, hk] += dvh
     return dq, dk, dv
+
+
+def decode_forward(q, k, v, causal: bool, scale: float, heads=None, workers: int = 1):
+    """Attention of Nq new queries against a key/value cache of Nk tokens.
+
+    q [B,Hq,Nq,d]; k, v [B,Hkv,Nk,d].  The queries are the last Nq tokens of the
+    sequence, so query i sits at position Nk - Nq + i and, when causal, sees the
+    keys j <= Nk - Nq + i.  Returns O [B,Hq,Nq,d] and LSE [B,Hq,Nq] (float64) for
+    every (b, hq) in ``heads`` (default: all; other entries NaN).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("expected [B, H, N, d] arrays")
+    b_, hq_, nq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != b_ or k.shape[3] != d or hq_ % k.shape[1] != 0:
+        raise ValueError(f"shape mismatch q{q.shape} k{k.shape} v{v.shape}")
+    hkv_, nk = k.shape[1], k.shape[2]
+    heads = [(b, h) for b in range(b_) for h in range(hq_)] if heads is None else list(heads)
+    off = _query_offset(nq, nk)
+    o = np.full(q.shape, np.nan)
+    lse = np.full(q.shape[:3], np.nan)
+    jobs = [(q[b, h], k[b, _group(h, hq_, hkv_)], v[b, _group(h, hq_, hkv_)], causal, scale, None, off)
+            for b, h in heads]
+    for (b, h), (ob, lb) in zip(heads, _run(_fwd_unit, jobs, workers)):
+        o[b, h] = ob
+        lse[b, h] = lb
+    return o, lse
