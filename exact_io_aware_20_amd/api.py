@@ -21,6 +21,7 @@ FA_STATUS = {
 }
 ENTRY_POINTS = ("fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_workspace_bytes",
                 "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq",
+                "fa_decode_forward", "fa_decode_workspace_bytes", "fa_decode_split", "fa_decode_merge",
                 "fa_check_args", "fa_status_string")
 
 _lib = None
@@ -55,6 +56,13 @@ def load_library() -> ctypes.CDLL:
     lib.fa_backward_dq.restype = i
     lib.fa_backward_workspace_bytes.argtypes = [i, i, i]
     lib.fa_backward_workspace_bytes.restype = sz
+    lib.fa_decode_forward.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, vp]
+    lib.fa_decode_forward.restype = i
+    for fn in (lib.fa_decode_split, lib.fa_decode_merge):
+        fn.argtypes = lib.fa_decode_forward.argtypes
+        fn.restype = i
+    lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i]
     lib.fa_check_args.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -115,6 +123,38 @@ def _forward(fn, dtype, q, k, v, causal, scale, o, lse, stream):
     _require(lse, "lse", torch.float32, (B, Hq, N))
     code = getattr(lib, fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                             B, Hq, Hkv, N, d, int(causal), float(scale), _stream(stream))
+    _check(fn, code)
+    return o, lse
+
+
+def decode_workspace_bytes(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int) -> int:
+    return int(load_library().fa_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, d))
+
+
+def decode_forward(q, k, v, causal: bool, scale: float, o=None, lse=None, workspace=None, stream=None,
+                   step: str = "all"):
+    """bf16 forward of Nq new queries against an Nk-token key/value cache via
+    fa_decode_forward (step "all"), or only its split or merge kernel (fa_decode_split /
+    fa_decode_merge).  q [B,Hq,Nq,d]; k, v [B,Hkv,Nk,d].  Returns (o, lse)."""
+    fn = {"all": "fa_decode_forward", "split": "fa_decode_split", "merge": "fa_decode_merge"}[step]
+    lib = load_library()
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    _require(q, "q", torch.bfloat16, (B, Hq, Nq, d))
+    _require(k, "k", torch.bfloat16, (B, Hkv, Nk, d))
+    _require(v, "v", torch.bfloat16, (B, Hkv, Nk, d))
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _require(o, "o", torch.bfloat16, (B, Hq, Nq, d))
+    _require(lse, "lse", torch.float32, (B, Hq, Nq))
+    if workspace is None:
+        nbytes = decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, d)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    code = getattr(lib, fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                            B, Hq, Hkv, Nq, Nk, d, int(causal), float(scale), _stream(stream))
     _check(fn, code)
     return o, lse
 

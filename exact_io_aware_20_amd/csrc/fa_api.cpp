@@ -111,6 +111,29 @@ float kernel_scale_log2(float scale) {
     return s > 0.f ? s : 1.17549435e-38f;
 }
 
+fa_status check_decode_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale) {
+    fa_status s = check_shape(B, Hq, Hkv, Nk, d, causal, scale);
+    if (s != FA_OK) return s;
+    if (Nq < 1 || (causal && Nq > Nk)) return FA_ERR_SHAPE;
+    if (fa::decode_plan(B, Hq, Hkv, Nq, Nk, d).grid > kMaxGrid || (long long)B * Hq * Nq > kMaxGrid)
+        return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+fa_status check_decode(const void* q, const void* k, const void* v, const void* o, const void* lse,
+                       const void* workspace, size_t ws_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                       int causal, float scale) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    fa_status s = check_decode_shape(B, Hq, Hkv, Nq, Nk, d, causal, scale);
+    if (s != FA_OK) return s;
+    const size_t ws_need = fa::decode_plan(B, Hq, Hkv, Nq, Nk, d).workspace_bytes;
+    if (!workspace || !aligned16(workspace) || ws_bytes < ws_need) return FA_ERR_WORKSPACE;
+    const uintptr_t qb = (uintptr_t)B * Hq * Nq * d * 2, kb = (uintptr_t)B * Hkv * Nk * d * 2;
+    const Arg a[6] = {{q, qb, false}, {k, kb, false}, {v, kb, false}, {o, qb, true},
+                      {lse, (uintptr_t)B * Hq * Nq * 4, true}, {workspace, ws_need, true}};
+    return check_tensors(a, 6);
+}
+
 fa::FwdParams fwd_params(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                          int Hkv, int N, int causal, float scale) {
     fa::FwdParams p;
@@ -179,6 +202,59 @@ fa_status fa_forward_f32(const float* q, const float* k, const float* v, float* 
     return launched(fa::launch_fwd_f32(fwd_params(q, k, v, o, lse, B, Hq, Hkv, N, causal, scale), d, stream));
 }
 
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+    if (check_decode_shape(B, Hq, Hkv, Nq, Nk, d, 0, 1.f) != FA_OK) return 0;
+    return fa::decode_plan(B, Hq, Hkv, Nq, Nk, d).workspace_bytes;
+}
+
+static fa_status decode_call(int steps, const void* q, const void* k, const void* v, void* o, float* lse,
+                             void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk,
+                             int d, int causal, float scale, hipStream_t stream) {
+    fa_status s = check_decode(q, k, v, o, lse, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, d, causal, scale);
+    if (s != FA_OK) return s;
+    const fa::DecodePlan pl = fa::decode_plan(B, Hq, Hkv, Nq, Nk, d);
+    fa::DecodeParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.part_o = (float*)workspace;
+    p.part_lse = (float*)workspace + (size_t)pl.nsplit * B * Hq * Nq * d;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Nq = Nq;
+    p.Nk = Nk;
+    p.causal = causal;
+    p.nrb = pl.nrb;
+    p.nsplit = pl.nsplit;
+    p.tiles_per_split = pl.tiles_per_split;
+    p.scale_log2 = kernel_scale_log2(scale);
+    return launched(fa::launch_decode(p, d, steps, stream));
+}
+
+fa_status fa_decode_forward(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                            size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                            float scale, hipStream_t stream) {
+    return decode_call(fa::kDecodeSplit | fa::kDecodeMerge, q, k, v, o, lse, workspace, workspace_bytes, B, Hq,
+                       Hkv, Nq, Nk, d, causal, scale, stream);
+}
+
+fa_status fa_decode_split(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                          size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                          float scale, hipStream_t stream) {
+    return decode_call(fa::kDecodeSplit, q, k, v, o, lse, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, d,
+                       causal, scale, stream);
+}
+
+fa_status fa_decode_merge(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                          size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                          float scale, hipStream_t stream) {
+    return decode_call(fa::kDecodeMerge, q, k, v, o, lse, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, d,
+                       causal, scale, stream);
+}
+
 size_t fa_backward_workspace_bytes(int B, int Hq, int N) { return workspace_bytes(B, Hq, N); }
 
 fa_status fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -235,7 +311,7 @@ const char* fa_status_string(fa_status status) {
         case FA_ERR_SCALE: return "scale must be finite and >= 0";
         case FA_ERR_ALIGN: return "every pointer must be 16-byte aligned";
         case FA_ERR_FLAG: return "causal must be 0 or 1";
-        case FA_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than fa_backward_workspace_bytes";
+        case FA_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than the required workspace bytes";
         case FA_ERR_ALIAS: return "an output overlaps an input or another output";
         case FA_ERR_LAUNCH: return "kernel launch failed";
     }

@@ -142,17 +142,22 @@ struct TileDma {
             off[k] = (row * D + ((pos % S::CHUNKS) ^ (uint32_t)S::swz((int)row)) * 8) * 2;
         }
     }
+    // all 64 rows of src are in bounds
+    __device__ __forceinline__ void issue_full(const uint16_t* src, uint16_t* lds_tile, int wave) const {
+        const char* base = (const char*)src;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = wave + k * NWAVES;
+            if (S::WAVE_LOADS % NWAVES == 0 || i < S::WAVE_LOADS)
+                __builtin_amdgcn_global_load_lds((const uint16_t*)(base + off[k]),
+                                                 (lds_void*)(lds_tile + i * 64 * 8), 16, 0, 0);
+        }
+    }
     // rows at or past `nvalid` are read from row nvalid-1 (in bounds, never used)
     __device__ __forceinline__ void issue(const uint16_t* src, int nvalid, uint16_t* lds_tile, int wave) const {
         const char* base = (const char*)src;
         if (nvalid >= 64) {
-#pragma unroll
-            for (int k = 0; k < PER; ++k) {
-                const int i = wave + k * NWAVES;
-                if (S::WAVE_LOADS % NWAVES == 0 || i < S::WAVE_LOADS)
-                    __builtin_amdgcn_global_load_lds((const uint16_t*)(base + off[k]),
-                                                     (lds_void*)(lds_tile + i * 64 * 8), 16, 0, 0);
-            }
+            issue_full(src, lds_tile, wave);
         } else {
 #pragma unroll
             for (int k = 0; k < PER; ++k) {

@@ -33,12 +33,38 @@ struct BwdParams {
     float scale_log2;
 };
 
+// Decode: Nq queries per head against Nk cached keys, the key range cut into
+// `nsplit` splits of `tiles_per_split` 64-key tiles, each split's result merged by
+// its log-sum-exp.
+struct DecodeParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    float* part_o;      // workspace: fp32 [nsplit][B*Hq*Nq][d], each split's normalised O
+    float* part_lse;    // workspace: fp32 [nsplit][B*Hq*Nq], each split's LSE in base 2
+    int B, Hq, Hkv, Nq, Nk, causal;
+    int nrb;            // 32-row blocks of the G*Nq packed query rows of a KV head
+    int nsplit, tiles_per_split;
+    float scale_log2;
+};
+
+struct DecodePlan {
+    int nrb, nsplit, tiles_per_split;
+    long long grid;           // workgroups of the split kernel
+    size_t workspace_bytes;
+};
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+
 long long fwd_bf16_grid(int B, int Hq, int N, int d);
 long long fwd_f32_grid(int B, int Hq, int N);
 long long bwd_grid_max(int B, int Hq, int Hkv, int N, int d);
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t stream);
+enum DecodeSteps { kDecodeSplit = 1, kDecodeMerge = 2 };
+hipError_t launch_decode(const DecodeParams& p, int d, int steps, hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t stream);

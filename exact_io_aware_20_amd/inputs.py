@@ -14,10 +14,15 @@ causal_n2048_d64              4    16   16   2048   64  yes     bf16   fwd (+LSE
 causal_n8192_d128             2    32   32   8192  128  yes     bf16   fwd, bwd
 gqa_n4096_d128                8    24    2   4096  128  yes     bf16   fwd, bwd
 longctx_n65536_d128           1    16   16  65536  128  both    bf16   fwd
+decode_gqa_kv65536_d128       8    24    2  65536  128  yes     bf16   decode, Nq=1
+decode_spec4_kv65536_d128     8    24    2  65536  128  yes     bf16   decode, Nq=4
 ==========================  ====  ===  ===  =====  ===  ======  =====  ===========
 
 The long-context workload multiplies q and k by 8 before the cast (a power of two,
 exact in bf16), so logits reach |x| ~ 500 and stress the running-max rescaling.
+The decode workloads hold a cache of N = 65536 keys and values per KV head and
+Nq = 1 (one new token) or Nq = 4 (four tokens checked at once) queries per query
+head; q is [B, Hq, Nq, d] and k, v are [B, Hkv, N, d].
 """
 from __future__ import annotations
 
@@ -41,6 +46,11 @@ class Workload:
     backward: bool
     qk_mult: float = 1.0
     extra: dict = field(default_factory=dict)
+    nq: int = 0            # decode: query rows per head (0: the queries are the whole sequence)
+
+    @property
+    def decode(self) -> bool:
+        return self.nq > 0
 
     @property
     def scale(self) -> float:
@@ -59,6 +69,8 @@ WORKLOADS = {
         Workload("gqa_n4096_d128", 4000, 8, 24, 2, 4096, 128, (True,), "bf16", True),
         Workload("longctx_n65536_d128", 5000, 1, 16, 16, 65536, 128, (True, False), "bf16",
                  False, qk_mult=8.0),
+        Workload("decode_gqa_kv65536_d128", 6000, 8, 24, 2, 65536, 128, (True,), "bf16", False, nq=1),
+        Workload("decode_spec4_kv65536_d128", 7000, 8, 24, 2, 65536, 128, (True,), "bf16", False, nq=4),
     )
 }
 
@@ -74,18 +86,20 @@ def seeded_normal(shape, seed: int, dtype=torch.bfloat16, mult: float = 1.0) -> 
 
 
 def make_inputs(B, Hq, Hkv, N, d, seed_base: int, dtype=torch.bfloat16, qk_mult: float = 1.0,
-                with_do: bool = False) -> dict:
-    """q [B,Hq,N,d], k and v [B,Hkv,N,d] (and dO [B,Hq,N,d]) on the CPU."""
+                with_do: bool = False, nq: int = 0) -> dict:
+    """q [B,Hq,Nq,d], k and v [B,Hkv,N,d] (and dO like q) on the CPU; Nq = nq, or N
+    when nq is 0."""
+    nq = nq or N
     out = {
-        "q": seeded_normal((B, Hq, N, d), seed_base + 1, dtype, qk_mult),
+        "q": seeded_normal((B, Hq, nq, d), seed_base + 1, dtype, qk_mult),
         "k": seeded_normal((B, Hkv, N, d), seed_base + 2, dtype, qk_mult),
         "v": seeded_normal((B, Hkv, N, d), seed_base + 3, dtype),
     }
     if with_do:
-        out["do"] = seeded_normal((B, Hq, N, d), seed_base + 4, dtype)
+        out["do"] = seeded_normal((B, Hq, nq, d), seed_base + 4, dtype)
     return out
 
 
 def workload_inputs(w: Workload, with_do: bool | None = None) -> dict:
     return make_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed_base, w.torch_dtype, w.qk_mult,
-                       w.backward if with_do is None else with_do)
+                       w.backward if with_do is None else with_do, w.nq)

@@ -59,3 +59,20 @@ def score_matrix_bytes(N, elt: int = 4, heads: int = 1, batch: int = 1) -> int:
 def kv_storage_saving(Hq, Hkv) -> float:
     """Fraction of K/V storage saved by Hkv shared heads versus Hq (MHA)."""
     return 1.0 - Hkv / Hq
+
+
+def decode_bytes(B, Hq, Hkv, Nq, Nk, d, elt: int) -> int:
+    """Decode call: read Q and the K/V cache once, write O and the fp32 LSE once."""
+    return elt * (2 * B * Hq * Nq * d + 2 * B * Hkv * Nk * d) + 4 * B * Hq * Nq
+
+
+def decode_split_bytes(B, Hq, Hkv, Nq, Nk, d, elt: int) -> int:
+    """The split kernel's algorithmic traffic: Q and the K/V cache read once (per
+    (batch, KV head, key) unit: 2 d elt bytes of K and V)."""
+    return elt * (B * Hq * Nq * d + 2 * B * Hkv * Nk * d)
+
+
+def decode_flops(B, Hq, Nq, Nk, d) -> float:
+    """Two Nq x Nk x d contractions per query head (the causal mask hides at most
+    Nq - 1 keys of Nk, so the full count is used)."""
+    return 4.0 * B * Hq * Nq * Nk * d

@@ -25,7 +25,8 @@ import sys
 from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("fa_fwd.hip", "fa_bwd.hip", "fa_common.hpp", "fa_launch.hpp")
+KERNEL_SOURCES = ("fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_fwd_tile.hpp", "fa_common.hpp",
+                  "fa_launch.hpp")
 TRAFFIC_TAG = "traffic-json:"
 
 

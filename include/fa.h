@@ -128,6 +128,52 @@ fa_status fa_backward_dq(const void* q, const void* k, const void* v, const void
                          hipStream_t stream);
 
 /*
+ * Decode forward: Nq new queries per head against a cache of Nk keys and values.
+ *
+ * The queries are the last Nq tokens of a sequence whose Nk keys and values, their
+ * own included, are all in the cache (Stanford lecture summary, "衡量并优化推理":
+ * decoding reuses the keys and values of earlier tokens).  Query i sits at
+ * position Nk - Nq + i; when causal it sees keys j <= Nk - Nq + i, otherwise all
+ * Nk keys.  With Nq = Nk this is exactly fa_forward.  Per query row:
+ *     O[b,hq,i,:] = sum_j softmax_j(s_ij) V[b,g,j,:],  LSE[b,hq,i] = log sum_j exp(s_ij)
+ * with s_ij and g as above.
+ *   q [B,Hq,Nq,d] bf16, k and v [B,Hkv,Nk,d] bf16 (read only); o [B,Hq,Nq,d] bf16
+ *   and lse [B,Hq,Nq] fp32 are overwritten.  Nq >= 1, Nk >= 1, and Nq <= Nk
+ *   when causal (FA_ERR_SHAPE otherwise); other rules as for fa_forward.
+ *   workspace: device memory of at least fa_decode_workspace_bytes(...) bytes
+ *   (passed in workspace_bytes), 16-byte aligned, clobbered by the call; it holds
+ *   the partial results of the key ranges the cache is cut into, which a second
+ *   kernel merges by their log-sum-exp.
+ * Bound by HBM bandwidth: every K and V byte is read once per call, shared by
+ * the Hq/Hkv query heads of its group.
+ */
+fa_status fa_decode_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+                            void* workspace, size_t workspace_bytes,
+                            int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                            hipStream_t stream);
+
+/* Bytes of device workspace fa_decode_forward needs for these sizes (it depends on
+ * the sizes only); 0 for invalid sizes. */
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+
+/*
+ * The two kernels fa_decode_forward enqueues, in this order, exposed so that a
+ * caller can time or place each one: fa_decode_split computes every key range's
+ * partial result into the workspace, fa_decode_merge combines them into o and lse.
+ * Both take fa_decode_forward's arguments and rules, and the merge must follow a
+ * split with the same arguments and workspace.  When the sizes give a single key
+ * range, the split writes o and lse itself and the merge enqueues nothing.
+ */
+fa_status fa_decode_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes,
+                          int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                          hipStream_t stream);
+fa_status fa_decode_merge(const void* q, const void* k, const void* v, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes,
+                          int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                          hipStream_t stream);
+
+/*
  * Host-only validation of a forward call, exactly as fa_forward performs it
  * (pointer presence, alignment and overlap, shapes, flag, scale), for an
  * element size elt_bytes of 2 (bf16) or 4 (fp32).  Touches no device memory

@@ -119,3 +119,50 @@ def test_backward_steps_reject_before_launch():
     assert lib.fa_backward_dkdv(Q, K, V, dO, ws, need, dk, dv, 1, 2, 1, 16, 64, 2, 0.1, None) == 7
     assert lib.fa_backward_dq(Q, K, V, dO, ws, need, Q, 1, 2, 1, 16, 64, 1, 0.1, None) == 9
     assert lib.fa_backward_dq(Q, K, V, dO, ws, need, dq, 1, 3, 2, 16, 64, 1, 0.1, None) == 3
+
+
+def test_decode_workspace_bytes():
+    lib = api.load_library()
+    # one fp32 row of d partial outputs plus one partial LSE per query row and key split
+    for B, Hq, Hkv, Nq, Nk, d in ((8, 24, 2, 1, 65536, 128), (2, 8, 1, 5, 1000, 64), (1, 1, 1, 1, 1, 64),
+                                  (4, 32, 8, 4, 32768, 128)):
+        nb = lib.fa_decode_workspace_bytes(B, Hq, Hkv, Nq, Nk, d)
+        per_split = B * Hq * Nq * (d + 1) * 4
+        assert nb > 0 and nb % per_split == 0
+        assert 1 <= nb // per_split <= (Nk + 63) // 64
+    assert lib.fa_decode_workspace_bytes(0, 1, 1, 1, 8, 64) == 0
+    assert lib.fa_decode_workspace_bytes(1, 3, 2, 1, 8, 64) == 0
+    assert lib.fa_decode_workspace_bytes(1, 1, 1, 0, 8, 64) == 0
+    assert lib.fa_decode_workspace_bytes(1, 1, 1, 1, 8, 80) == 0
+
+
+def test_decode_rejects_before_launch():
+    lib = api.load_library()
+    ws = 0x60_0000_0000
+    args = lambda q=Q, o=O, lse=L, ws_=ws, wsb=None, **kw: lib.fa_decode_forward(
+        q, K, V, o, lse, ws_,
+        lib.fa_decode_workspace_bytes(kw.get("B", 1), kw.get("Hq", 4), kw.get("Hkv", 2), kw.get("Nq", 2),
+                                      kw.get("Nk", 100), kw.get("d", 64)) if wsb is None else wsb,
+        kw.get("B", 1), kw.get("Hq", 4), kw.get("Hkv", 2), kw.get("Nq", 2), kw.get("Nk", 100), kw.get("d", 64),
+        kw.get("causal", 1), kw.get("scale", 0.125), None)
+    assert args(q=None) == 1
+    assert args(ws_=None) == 8
+    assert args(wsb=16) == 8
+    assert args(ws_=ws + 4) == 8
+    assert args(Nq=0) == 2
+    assert args(Nq=101) == 2          # causal: the queries must be the tail of the cache
+    assert args(Hq=3) == 3
+    assert args(d=96) == 4
+    assert args(causal=2) == 7
+    assert args(scale=float("nan")) == 5
+    assert args(o=Q) == 9             # o aliases q
+    assert args(ws_=K) == 9           # workspace aliases k
+
+
+def test_decode_steps_reject_before_launch():
+    lib = api.load_library()
+    need = lib.fa_decode_workspace_bytes(1, 4, 2, 2, 100, 64)
+    for fn in (lib.fa_decode_split, lib.fa_decode_merge):
+        assert fn(Q, K, V, O, L, 0x60_0000_0000, need - 4, 1, 4, 2, 2, 100, 64, 1, 0.1, None) == 8
+        assert fn(Q, K, V, O, O, 0x60_0000_0000, need, 1, 4, 2, 2, 100, 64, 1, 0.1, None) == 9
+        assert fn(Q, K, V, O, L, 0x60_0000_0000, need, 1, 4, 2, 200, 100, 64, 1, 0.1, None) == 2
