@@ -17,8 +17,9 @@
 //     further row blocks, which read the same K/V through L2.
 //   * The key range is cut into splits of whole 64-key tiles so that the grid fills
 //     the chip even for one sequence; each split is one single-wave workgroup with
-//     its own 32 KB (d = 128) of LDS, so five run per CU and their direct
-//     global->LDS loads keep enough bytes in flight.  Inside a split the per-tile
+//     its own 32 KB (d = 128) of LDS.  About 1024 splits are made, one wave per SIMD:
+//     a fifth wave per CU (LDS would allow it) shares a SIMD with another and
+//     measured slower than four.  Inside a split the per-tile
 //     steps are those of the full-sequence forward: S^T = K Q^T on the matrix
 //     cores, the lazily rescaled online softmax, O^T += V^T P^T.
 //   * Each split writes its normalised partial output and its base-2 log-sum-exp;
@@ -33,7 +34,7 @@
 namespace fa {
 
 constexpr int kDecodeTile = 64;           // keys per K/V tile
-constexpr int kDecodeTargetWgs = 1280;    // five single-wave workgroups per CU on 256 CUs
+constexpr int kDecodeTargetWgs = 1024;    // one single-wave workgroup per SIMD: four per CU on 256 CUs
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8); the counters not named are left at their maximum.
