@@ -36,6 +36,10 @@ Readings where the pages are silent (each listed with its reason in the design n
   and values of earlier tokens instead of recomputing them).  Query i therefore sits
   at position Nk - Nq + i, and causally sees keys j <= Nk - Nq + i; with Nq = Nk
   this is the ordinary causal mask.
+* Sliding window (``window`` >= 0; page "ZeRO 与 FlashAttention 各优化什么?", section
+  "注意力瓶颈与优化路线": a sliding window restricts which positions a query sees):
+  query position i sees key j only if |i - j| <= window, on top of the causal rule,
+  so a causal row sees its window + 1 most recent keys.  window < 0 means no window.
 * The gradients are the analytic softmax-Jacobian gradients (the pages print none):
       dP = dO V^T,  D_i = sum_j P_ij dP_ij,  dS = P * (dP - D),
       dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO,
@@ -67,14 +71,17 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def _scores(q_rows: np.ndarray, k: np.ndarray, rows: np.ndarray, causal: bool, scale: float):
-    """S for the given query rows against all keys, with the causal mask applied.
+def _scores(q_rows: np.ndarray, k: np.ndarray, rows: np.ndarray, causal: bool, scale: float, window: int = -1):
+    """S for the given query rows against all keys, with the causal mask (key <= query)
+    and, for window >= 0, the sliding-window mask (|query - key| <= window) applied.
 
     ``rows`` are the queries' positions in the key sequence."""
     s = scale * (q_rows @ k.T)
+    cols = np.arange(k.shape[0])
     if causal:
-        cols = np.arange(k.shape[0])
         s = np.where(cols[None, :] <= rows[:, None], s, -np.inf)
+    if window >= 0:
+        s = np.where(np.abs(cols[None, :] - rows[:, None]) <= window, s, -np.inf)
     return s
 
 
@@ -83,12 +90,13 @@ def _query_offset(nq: int, nk: int) -> int:
     return nk - nq
 
 
-def head_forward(q, k, v, causal: bool, scale: float, rows=None, offset: int = 0):
+def head_forward(q, k, v, causal: bool, scale: float, rows=None, offset: int = 0, window: int = -1):
     """One query head: O and LSE for the selected query rows (default: all rows).
 
     q: [Nq, d]; k, v: [Nk, d] (the KV head of this query's group); query row i sits
     at position i + offset of the key sequence (offset 0 when queries and keys are
-    the same sequence).  Returns (O [len(rows), d], LSE [len(rows)]) in float64.  A
+    the same sequence); ``window`` >= 0 adds the sliding-window mask.  Returns
+    (O [len(rows), d], LSE [len(rows)]) in float64.  A
     row with no visible key (not reachable when the queries are the tail of the key
     sequence) gives O = 0 and LSE = -inf.
     """
@@ -99,7 +107,7 @@ def head_forward(q, k, v, causal: bool, scale: float, rows=None, offset: int = 0
     lse = np.full(rows.size, -np.inf)
     for b0 in range(0, rows.size, ROW_BLOCK):
         r = rows[b0:b0 + ROW_BLOCK]
-        s = _scores(q[r], k, r + offset, causal, scale)
+        s = _scores(q[r], k, r + offset, causal, scale, window)
         m = s.max(axis=1)                              # pass 1: row max
         ok = np.isfinite(m)
         e = np.exp(s - np.where(ok, m, 0.0)[:, None])  # pass 2: exponentials
@@ -110,17 +118,17 @@ def head_forward(q, k, v, causal: bool, scale: float, rows=None, offset: int = 0
     return o, lse
 
 
-def head_probs(q, k, causal: bool, scale: float):
+def head_probs(q, k, causal: bool, scale: float, window: int = -1):
     """The full softmax matrix P [N, N] of one head (small inputs only)."""
     q, k = _f64(q), _f64(k)
     rows = np.arange(q.shape[0])
-    s = _scores(q, k, rows, causal, scale)
+    s = _scores(q, k, rows, causal, scale, window)
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)
     return e / e.sum(axis=1, keepdims=True)
 
 
-def head_backward(q, k, v, do, causal: bool, scale: float):
+def head_backward(q, k, v, do, causal: bool, scale: float, window: int = -1):
     """One query head: (dQ, dK, dV) for L = sum(dO * O), float64.
 
     dK and dV are this head's contribution to its KV head; the caller sums them
@@ -133,7 +141,7 @@ def head_backward(q, k, v, do, causal: bool, scale: float):
     dv = np.zeros_like(v)
     for b0 in range(0, n, ROW_BLOCK):
         r = np.arange(b0, min(n, b0 + ROW_BLOCK))
-        s = _scores(q[r], k, r, causal, scale)
+        s = _scores(q[r], k, r, causal, scale, window)
         m = s.max(axis=1, keepdims=True)
         e = np.exp(s - m)
         p = e / e.sum(axis=1, keepdims=True)          # P, full rows
@@ -164,13 +172,13 @@ def _check_shapes(q, k, v):
 
 
 def _fwd_unit(args):
-    q, k, v, causal, scale, rows, offset = args
-    return head_forward(q, k, v, causal, scale, rows, offset)
+    q, k, v, causal, scale, rows, offset, window = args
+    return head_forward(q, k, v, causal, scale, rows, offset, window)
 
 
 def _bwd_unit(args):
-    q, k, v, do, causal, scale = args
-    return head_backward(q, k, v, do, causal, scale)
+    q, k, v, do, causal, scale, window = args
+    return head_backward(q, k, v, do, causal, scale, window)
 
 
 @contextlib.contextmanager
@@ -198,7 +206,8 @@ def _run(fn, jobs, workers: int):
     return [fn(j) for j in jobs]
 
 
-def attention_forward(q, k, v, causal: bool, scale: float, heads=None, rows=None, workers: int = 1):
+def attention_forward(q, k, v, causal: bool, scale: float, heads=None, rows=None, workers: int = 1,
+                      window: int = -1):
     """O [B,Hq,N,d] and LSE [B,Hq,N] (float64) for every (b, hq) in ``heads``.
 
     ``heads`` is an iterable of (b, hq) pairs (default: all); entries of heads not
@@ -212,7 +221,7 @@ def attention_forward(q, k, v, causal: bool, scale: float, heads=None, rows=None
     heads = [(b, h) for b in range(b_) for h in range(hq_)] if heads is None else list(heads)
     o = np.full(q.shape, np.nan)
     lse = np.full(q.shape[:3], np.nan)
-    jobs = [(q[b, h], k[b, _group(h, hq_, hkv_)], v[b, _group(h, hq_, hkv_)], causal, scale, rows, 0)
+    jobs = [(q[b, h], k[b, _group(h, hq_, hkv_)], v[b, _group(h, hq_, hkv_)], causal, scale, rows, 0, window)
             for b, h in heads]
     results = _run(_fwd_unit, jobs, workers)
     sel = slice(None) if rows is None else np.asarray(rows)
@@ -222,7 +231,8 @@ def attention_forward(q, k, v, causal: bool, scale: float, heads=None, rows=None
     return o, lse
 
 
-def attention_backward(q, k, v, do, causal: bool, scale: float, groups=None, workers: int = 1):
+def attention_backward(q, k, v, do, causal: bool, scale: float, groups=None, workers: int = 1,
+                       window: int = -1):
     """dQ [B,Hq,N,d], dK and dV [B,Hkv,N,d] (float64) for the listed (b, hkv) groups.
 
     A group's dK/dV is the sum over its Hq/Hkv query heads; the dQ of every query
@@ -238,7 +248,7 @@ def attention_backward(q, k, v, do, causal: bool, scale: float, groups=None, wor
     dk = np.full(k.shape, np.nan)
     dv = np.full(v.shape, np.nan)
     units = [(b, hk, h) for b, hk in groups for h in range(hk * g, hk * g + g)]
-    jobs = [(q[b, h], k[b, hk], v[b, hk], do[b, h], causal, scale) for b, hk, h in units]
+    jobs = [(q[b, h], k[b, hk], v[b, hk], do[b, h], causal, scale, window) for b, hk, h in units]
     results = _run(_bwd_unit, jobs, workers)
     for b, hk in groups:
         dk[b, hk] = 0.0
@@ -269,7 +279,7 @@ def decode_forward(q, k, v, causal: bool, scale: float, heads=None, workers: int
     off = _query_offset(nq, nk)
     o = np.full(q.shape, np.nan)
     lse = np.full(q.shape[:3], np.nan)
-    jobs = [(q[b, h], k[b, _group(h, hq_, hkv_)], v[b, _group(h, hq_, hkv_)], causal, scale, None, off)
+    jobs = [(q[b, h], k[b, _group(h, hq_, hkv_)], v[b, _group(h, hq_, hkv_)], causal, scale, None, off, -1)
             for b, h in heads]
     for (b, h), (ob, lb) in zip(heads, _run(_fwd_unit, jobs, workers)):
         o[b, h] = ob
