@@ -17,11 +17,12 @@ LIB_PATH = Path(os.environ.get("FA_MI355X_LIB", Path(__file__).resolve().parent 
 FA_STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_GQA", 4: "FA_ERR_HEADDIM",
     5: "FA_ERR_SCALE", 6: "FA_ERR_ALIGN", 7: "FA_ERR_FLAG", 8: "FA_ERR_WORKSPACE",
-    9: "FA_ERR_ALIAS", 10: "FA_ERR_LAUNCH",
+    9: "FA_ERR_ALIAS", 10: "FA_ERR_LAUNCH", 11: "FA_ERR_WINDOW",
 }
 ENTRY_POINTS = ("fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_workspace_bytes",
                 "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq",
                 "fa_decode_forward", "fa_decode_workspace_bytes", "fa_decode_split", "fa_decode_merge",
+                "fa_forward_window", "fa_backward_window", "fa_backward_dkdv_window", "fa_backward_dq_window",
                 "fa_check_args", "fa_status_string")
 
 _lib = None
@@ -63,6 +64,14 @@ def load_library() -> ctypes.CDLL:
         fn.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_forward_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    lib.fa_forward_window.restype = i
+    lib.fa_backward_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, vp]
+    lib.fa_backward_window.restype = i
+    lib.fa_backward_dkdv_window.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, i, i, i, f, vp]
+    lib.fa_backward_dkdv_window.restype = i
+    lib.fa_backward_dq_window.argtypes = [vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, i, i, f, vp]
+    lib.fa_backward_dq_window.restype = i
     lib.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i]
     lib.fa_check_args.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -99,8 +108,11 @@ def _require(t: torch.Tensor, name: str, dtype, shape):
                          f"got {t.dtype} {tuple(t.shape)} on {t.device} contiguous={t.is_contiguous()}")
 
 
-def forward(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None):
-    """bf16 forward via fa_forward.  Returns (o, lse); o bf16 [B,Hq,N,d], lse fp32 [B,Hq,N]."""
+def forward(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None, window=None):
+    """bf16 forward via fa_forward (or fa_forward_window when ``window`` is given).
+    Returns (o, lse); o bf16 [B,Hq,N,d], lse fp32 [B,Hq,N]."""
+    if window is not None:
+        return _forward("fa_forward_window", torch.bfloat16, q, k, v, causal, scale, o, lse, stream, window)
     return _forward("fa_forward", torch.bfloat16, q, k, v, causal, scale, o, lse, stream)
 
 
@@ -109,7 +121,7 @@ def forward_f32(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=No
     return _forward("fa_forward_f32", torch.float32, q, k, v, causal, scale, o, lse, stream)
 
 
-def _forward(fn, dtype, q, k, v, causal, scale, o, lse, stream):
+def _forward(fn, dtype, q, k, v, causal, scale, o, lse, stream, window=None):
     lib = load_library()
     B, Hq, Hkv, N, d = _shape(q, k)
     _require(q, "q", dtype, (B, Hq, N, d))
@@ -121,8 +133,9 @@ def _forward(fn, dtype, q, k, v, causal, scale, o, lse, stream):
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     _require(o, "o", dtype, (B, Hq, N, d))
     _require(lse, "lse", torch.float32, (B, Hq, N))
+    extra = () if window is None else (int(window),)
     code = getattr(lib, fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                            B, Hq, Hkv, N, d, int(causal), float(scale), _stream(stream))
+                            B, Hq, Hkv, N, d, int(causal), *extra, float(scale), _stream(stream))
     _check(fn, code)
     return o, lse
 
@@ -164,8 +177,9 @@ def workspace_bytes(B: int, Hq: int, N: int) -> int:
 
 
 def backward(q, k, v, o, do, lse, causal: bool, scale: float, dq=None, dk=None, dv=None,
-             workspace=None, stream=None):
-    """bf16 backward via fa_backward.  Returns (dq, dk, dv)."""
+             workspace=None, stream=None, window=None):
+    """bf16 backward via fa_backward (or fa_backward_window when ``window`` is given).
+    Returns (dq, dk, dv)."""
     lib = load_library()
     B, Hq, Hkv, N, d = _shape(q, k)
     for t, name, shp in ((q, "q", (B, Hq, N, d)), (k, "k", (B, Hkv, N, d)), (v, "v", (B, Hkv, N, d)),
@@ -181,17 +195,20 @@ def backward(q, k, v, o, do, lse, causal: bool, scale: float, dq=None, dk=None, 
     nbytes = workspace_bytes(B, Hq, N)
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    code = lib.fa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                           lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                           B, Hq, Hkv, N, d, int(causal), float(scale), _stream(stream))
-    _check("fa_backward", code)
+    fn = "fa_backward" if window is None else "fa_backward_window"
+    extra = () if window is None else (int(window),)
+    code = getattr(lib, fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                            B, Hq, Hkv, N, d, int(causal), *extra, float(scale), _stream(stream))
+    _check(fn, code)
     return dq, dk, dv
 
 
 def backward_steps(q, k, v, o, do, lse, causal: bool, scale: float, dq, dk, dv, workspace,
-                   stream=None, steps=("pre", "dkdv", "dq")):
-    """Enqueue the named backward steps (fa_backward_preprocess / _dkdv / _dq) in order.
+                   stream=None, steps=("pre", "dkdv", "dq"), window=None):
+    """Enqueue the named backward steps (fa_backward_preprocess / _dkdv / _dq, or the
+    _window forms of the last two when ``window`` is given) in order.
 
     Preallocated outputs and workspace are required; this is the form the benchmark
     uses to time each kernel on its own.
@@ -205,13 +222,17 @@ def backward_steps(q, k, v, o, do, lse, causal: bool, scale: float, dq, dk, dv, 
             code = lib.fa_backward_preprocess(o.data_ptr(), do.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
                                               wsb, B, Hq, N, d, st)
         elif step == "dkdv":
-            code = lib.fa_backward_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
-                                        workspace.data_ptr(), wsb, dk.data_ptr(), dv.data_ptr(),
-                                        B, Hq, Hkv, N, d, int(causal), float(scale), st)
+            fn = "fa_backward_dkdv" if window is None else "fa_backward_dkdv_window"
+            extra = () if window is None else (int(window),)
+            code = getattr(lib, fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                                    workspace.data_ptr(), wsb, dk.data_ptr(), dv.data_ptr(),
+                                    B, Hq, Hkv, N, d, int(causal), *extra, float(scale), st)
         elif step == "dq":
-            code = lib.fa_backward_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
-                                      workspace.data_ptr(), wsb, dq.data_ptr(),
-                                      B, Hq, Hkv, N, d, int(causal), float(scale), st)
+            fn = "fa_backward_dq" if window is None else "fa_backward_dq_window"
+            extra = () if window is None else (int(window),)
+            code = getattr(lib, fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                                    workspace.data_ptr(), wsb, dq.data_ptr(),
+                                    B, Hq, Hkv, N, d, int(causal), *extra, float(scale), st)
         else:
             raise ValueError(step)
         _check(f"fa_backward_{step}", code)

@@ -147,6 +147,7 @@ fa::FwdParams fwd_params(const void* q, const void* k, const void* v, void* o, f
     p.Hkv = Hkv;
     p.N = N;
     p.causal = causal;
+    p.window = -1;
     p.scale = scale;
     p.scale_log2 = kernel_scale_log2(scale);
     return p;
@@ -172,10 +173,14 @@ fa::BwdParams bwd_params(const void* q, const void* k, const void* v, const void
     p.Hkv = Hkv;
     p.N = N;
     p.causal = causal;
+    p.window = -1;
     p.scale = scale;
     p.scale_log2 = kernel_scale_log2(scale);
     return p;
 }
+
+// A window as wide as the sequence restricts nothing: the kernels take it as none.
+int kernel_window(int window, int N) { return window < N - 1 ? window : -1; }
 
 fa_status launched(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
 
@@ -269,6 +274,57 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
     return launched(fa::launch_bwd_dq(p, d, stream));
 }
 
+fa_status fa_forward_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                            int Hkv, int N, int d, int causal, int window, float scale, hipStream_t stream) {
+    if (window < 0) return FA_ERR_WINDOW;
+    fa_status s = check_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, 2);
+    if (s != FA_OK) return s;
+    fa::FwdParams p = fwd_params(q, k, v, o, lse, B, Hq, Hkv, N, causal, scale);
+    p.window = kernel_window(window, N);
+    return launched(fa::launch_fwd_bf16(p, d, stream));
+}
+
+fa_status fa_backward_window(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                             const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                             int B, int Hq, int Hkv, int N, int d, int causal, int window, float scale,
+                             hipStream_t stream) {
+    if (window < 0) return FA_ERR_WINDOW;
+    fa_status s = check_bwd(kAll, q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
+                            N, d, causal, scale);
+    if (s != FA_OK) return s;
+    fa::BwdParams p = bwd_params(q, k, v, o, dO, lse, dq, dk, dv, workspace, B, Hq, Hkv, N, causal, scale);
+    p.window = kernel_window(window, N);
+    if ((s = launched(fa::launch_bwd_pre(p, d, stream))) != FA_OK) return s;
+    if ((s = launched(fa::launch_bwd_dkdv(p, d, stream))) != FA_OK) return s;
+    return launched(fa::launch_bwd_dq(p, d, stream));
+}
+
+fa_status fa_backward_dkdv_window(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
+                                  size_t workspace_bytes, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+                                  int causal, int window, float scale, hipStream_t stream) {
+    if (window < 0) return FA_ERR_WINDOW;
+    fa_status s = check_bwd(kDkdv, q, k, v, nullptr, dO, nullptr, nullptr, dk, dv, workspace, workspace_bytes, B,
+                            Hq, Hkv, N, d, causal, scale);
+    if (s != FA_OK) return s;
+    fa::BwdParams p =
+        bwd_params(q, k, v, nullptr, dO, nullptr, nullptr, dk, dv, workspace, B, Hq, Hkv, N, causal, scale);
+    p.window = kernel_window(window, N);
+    return launched(fa::launch_bwd_dkdv(p, d, stream));
+}
+
+fa_status fa_backward_dq_window(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
+                                size_t workspace_bytes, void* dq, int B, int Hq, int Hkv, int N, int d, int causal,
+                                int window, float scale, hipStream_t stream) {
+    if (window < 0) return FA_ERR_WINDOW;
+    fa_status s = check_bwd(kDq, q, k, v, nullptr, dO, nullptr, dq, nullptr, nullptr, workspace, workspace_bytes, B,
+                            Hq, Hkv, N, d, causal, scale);
+    if (s != FA_OK) return s;
+    fa::BwdParams p =
+        bwd_params(q, k, v, nullptr, dO, nullptr, dq, nullptr, nullptr, workspace, B, Hq, Hkv, N, causal, scale);
+    p.window = kernel_window(window, N);
+    return launched(fa::launch_bwd_dq(p, d, stream));
+}
+
 fa_status fa_backward_preprocess(const void* o, const void* dO, const float* lse, void* workspace,
                                  size_t workspace_bytes, int B, int Hq, int N, int d, hipStream_t stream) {
     fa_status s = check_bwd(kPre, nullptr, nullptr, nullptr, o, dO, lse, nullptr, nullptr, nullptr,
@@ -314,6 +370,7 @@ const char* fa_status_string(fa_status status) {
         case FA_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than the required workspace bytes";
         case FA_ERR_ALIAS: return "an output overlaps an input or another output";
         case FA_ERR_LAUNCH: return "kernel launch failed";
+        case FA_ERR_WINDOW: return "window must be >= 0";
     }
     return "unknown status";
 }

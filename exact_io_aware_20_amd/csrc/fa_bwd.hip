@@ -89,14 +89,22 @@ __device__ __forceinline__ f32x16 qk_half(const uint16_t* nat, const u32x4 (&bf)
     return c;
 }
 
-// Set S to -inf where key > query (causal) or the query row is >= N, so that
-// 2^(S*sl2 - LSE2) is exactly 0 there.  Queries of register r: qrow0 + 8(r/4) + r%4.
-__device__ __forceinline__ void mask_half(f32x16& s, int qrow0, int key, int N, int causal) {
+// Set S to -inf where the query row is >= N or outside this key's band
+// key - wr <= query <= key + wl, so that 2^(S*sl2 - LSE2) is exactly 0 there.
+// Queries of register r: qrow0 + 8(r/4) + r%4.
+__device__ __forceinline__ void mask_half(f32x16& s, int qrow0, int key, int N, int wl, int wr) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int qq = qrow0 + 8 * (r >> 2) + (r & 3);
-        s[r] = (qq < N && (!causal || key <= qq)) ? s[r] : kNegInf;
+        s[r] = (qq < N && qq >= key - wr && qq <= key + wl) ? s[r] : kNegInf;
     }
+}
+
+// Reach of the visible band (key j visible to query i iff i - wl <= j <= i + wr):
+// without a window wl = N, i.e. no limit; causal means wr = 0.
+__device__ __forceinline__ int band_left(const BwdParams& p) { return p.window >= 0 ? p.window : p.N; }
+__device__ __forceinline__ int band_right(const BwdParams& p) {
+    return p.causal ? 0 : (p.window >= 0 ? p.window : p.N);
 }
 
 // Register 4g+i of a C tile (query 8g + 4hh + i of its half) packed as k-slot
@@ -163,9 +171,10 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, in
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) acc[db] = zero16();
 
-    const int nqt = (N + C::BQ - 1) / C::BQ;
-    const int qt_start = p.causal ? k0 / C::BQ : 0;
-    const int per_head = nqt - qt_start;
+    // query tiles holding a row that sees one of the workgroup's keys
+    const int wl = band_left(p), wr = band_right(p);
+    const int qt_start = max(0, k0 - wr) / C::BQ;
+    const int per_head = min(N - 1, k0 + C::BK - 1 + wl) / C::BQ + 1 - qt_start;
     const int nitems = G * per_head;
     const float sl2 = p.scale_log2;
     float* pbuf = (float*)(smem + C::NSTAGE * C::STAGE) + (wave & 3) * 32 * 64;   // this pair's P slots
@@ -187,7 +196,7 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, in
         }
     };
     // keys of this wave visible to some row of the item's tile
-    auto active = [&](int q0) { return kw0 < N && (!p.causal || q0 + C::BQ - 1 >= kw0); };
+    auto active = [&](int q0) { return kw0 < N && q0 + C::BQ - 1 >= kw0 - wr && q0 <= kw0 + 31 + wl; };
 
     if (nitems > 0) issue_item(0);
     for (int it = 0; it <= nitems; ++it) {
@@ -207,11 +216,11 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, in
         __builtin_amdgcn_s_setprio(PV ? 2 : 0);
         if (act) {
             if constexpr (PV) {
-                const bool mask = (p.causal && q0 < kw0 + 31) || (q0 + C::BQ > N);
+                const bool mask = q0 < kw0 + 31 - wr || q0 + C::BQ > N || q0 + C::BQ - 1 > kw0 + wl;
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
                     x[qb] = qk_half<D>(st, bfr, qb, l32, hh);
-                    if (mask) mask_half(x[qb], q0 + 32 * qb + 4 * hh, key, N, p.causal);
+                    if (mask) mask_half(x[qb], q0 + 32 * qb + 4 * hh, key, N, wl, wr);
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const f32x4 L = *(const f32x4*)(lse2 + 32 * qb + 8 * g + 4 * hh);
@@ -344,9 +353,12 @@ void fa_bwd_dq_kernel(BwdParams p) {
     const int qw0 = q0 + wave * 32;
     const int q = qw0 + l32;
     const int q_last = min(q0 + C::BR, N) - 1;
-    const int ntiles = p.causal ? q_last / C::BC + 1 : (N + C::BC - 1) / C::BC;
+    // tiles [t_begin, ntiles) hold a key visible to some row of the workgroup
+    const int wl = band_left(p), wr = band_right(p);
+    const int t_begin = max(0, q0 - wl) / C::BC;
+    const int ntiles = min(N - 1, q_last + wr) / C::BC + 1;
     const int wq_last = min(qw0 + 32, N) - 1;
-    const int wave_tiles = wq_last < qw0 ? 0 : (p.causal ? wq_last / C::BC + 1 : ntiles);
+    const int wave_tiles = wq_last < qw0 ? 0 : min(N - 1, wq_last + wr) / C::BC + 1;
 
     // Q and dO as B operands of S^T = K Q^T and dP^T = V dO^T (lane: query)
     u32x4 qf[C::DC], gf[C::DC];
@@ -373,8 +385,8 @@ void fa_bwd_dq_kernel(BwdParams p) {
         vdma.issue(Vh + (size_t)k0 * D, N - k0, st + C::KT, wave);
     };
 
-    load_tile(0, smem);
-    for (int t = 0; t < ntiles; ++t) {
+    load_tile(t_begin, smem + (t_begin & 1) * C::STAGE);
+    for (int t = t_begin; t < ntiles; ++t) {
         const int k0 = t * C::BC;
         const uint16_t* st = smem + (t & 1) * C::STAGE;
         __builtin_amdgcn_s_waitcnt(0);
@@ -390,13 +402,14 @@ void fa_bwd_dq_kernel(BwdParams p) {
                     s[kb] = mfma32x32x16(lds16(st + KS::at(32 * kb + l32, 2 * c + hh)), qf[c], s[kb]);
                     dp[kb] = mfma32x32x16(lds16(st + C::KT + VS::at(32 * kb + l32, 2 * c + hh)), gf[c], dp[kb]);
                 }
-            if ((p.causal && k0 + C::BC - 1 > qw0) || (k0 + C::BC > N)) {
+            if (k0 + C::BC - 1 > qw0 + wr || k0 + C::BC > N || k0 < wq_last - wl) {
+                const int lo = q - wl, hi = min(q + wr, N - 1);
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                        const bool vis = kk < N && (!p.causal || kk <= q);
+                        const bool vis = kk >= lo && kk <= hi;
                         s[kb][r] = vis ? s[kb][r] : kNegInf;   // -inf * sl2 - lse2 -> p = 0
                     }
             }

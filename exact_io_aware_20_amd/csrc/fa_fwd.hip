@@ -48,7 +48,7 @@ struct FwdCfg {
 // The leading steps, whose current and next tiles are fully visible to every row
 // of the workgroup, run as branch-free blocks in a loop of their own; the
 // diagonal and ragged tail steps take the general path.
-template <int D>
+template <int D, bool WINDOW>
 __global__ __launch_bounds__(FwdCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_bf16_kernel(FwdParams p) {
     using C = FwdCfg<D>;
@@ -65,6 +65,10 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     const int l32 = lane & 31;
     const int hh = lane >> 5;
     const int N = p.N;
+    // Visible band: key j is visible to query i iff i - wl <= j <= i + wr (and j < N).
+    // Without a window wl = N (no lower limit); causal means wr = 0.
+    const int wl = WINDOW ? p.window : N;
+    const int wr = p.causal ? 0 : (WINDOW ? p.window : N);
 
     const int ntile_q = (N + C::BR - 1) / C::BR;
     int head, qt;
@@ -81,9 +85,11 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     const int qw0 = q0 + wave * 32;
     const int q = qw0 + l32;
     const int q_last = min(q0 + C::BR, N) - 1;
-    const int ntiles = p.causal ? q_last / C::BC + 1 : (N + C::BC - 1) / C::BC;
+    // tiles [t_begin, ntiles) hold a key visible to some row of the workgroup
+    const int t_begin = WINDOW ? max(0, q0 - wl) / C::BC : 0;
+    const int ntiles = min(N - 1, q_last + wr) / C::BC + 1;
     const int wq_last = min(qw0 + 32, N) - 1;
-    const int wave_tiles = wq_last < qw0 ? 0 : (p.causal ? wq_last / C::BC + 1 : ntiles);
+    const int wave_tiles = wq_last < qw0 ? 0 : min(N - 1, wq_last + wr) / C::BC + 1;
 
     // Q fragments: B operand of S^T = K Q^T (lane: query, slots: 8 consecutive d).
     u32x4 qf[C::DC];
@@ -104,14 +110,15 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     auto issue_k = [&](int t, uint16_t* buf) { kdma.issue(Kh + (size_t)t * C::BC * D, N - t * C::BC, buf, wave); };
     auto issue_v = [&](int t, uint16_t* buf) { vdma.issue(Vh + (size_t)t * C::BC * D, N - t * C::BC, buf, wave); };
 
-    // prologue: K(0), V(0) -> LDS; S(0); K(1) -> LDS
-    issue_k(0, kbuf);
-    issue_v(0, vbuf);
+    // prologue: K(t0), V(t0) -> LDS; S(t0); K(t0+1) -> LDS (buffers by tile parity)
+    const int tb = t_begin & 1;
+    issue_k(t_begin, kbuf + tb * KB);
+    issue_v(t_begin, vbuf + tb * VB);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16 sa[2], sb[2];
-    if (0 < wave_tiles) fwd_scores<D>(kbuf, qf, sa, l32, hh);
-    if (1 < ntiles) issue_k(1, kbuf + KB);
+    if (t_begin < wave_tiles) fwd_scores<D>(kbuf + tb * KB, qf, sa, l32, hh);
+    if (t_begin + 1 < ntiles) issue_k(t_begin + 1, kbuf + (tb ^ 1) * KB);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -142,7 +149,8 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         if (t + 1 < ntiles) issue_v(t + 1, vbuf + ((t + 1) & 1) * VB);
         if (t + 1 < wave_tiles) fwd_scores<D>(kbuf + ((t + 1) & 1) * KB, qf, nxt, l32, hh);
         if (t < wave_tiles) {
-            if ((p.causal && k0 + C::BC - 1 > qw0) || (k0 + C::BC > N)) fwd_mask(cur, k0, q, N, p.causal, hh);
+            if (k0 + C::BC - 1 > qw0 + wr || k0 + C::BC > N || (WINDOW && k0 < wq_last - wl))
+                fwd_mask<WINDOW>(cur, k0, q - wl, min(q + wr, N - 1), hh);
             fwd_rescale<D>(cur, o, m_ref, l_part, sl2);
             u32x4 pf[2][2];
             fwd_probs(cur, m_ref, sl2, pf, l_part);
@@ -151,10 +159,29 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
-    // steps 0 .. nfast-1 are fast for every wave (wave 0 has the fewest visible tiles)
-    const int full_wg = p.causal ? (q0 + 1) / C::BC : N / C::BC;
-    const int nfast = max(0, min(full_wg, ntiles) - 1);
-    int t = 0;
+    // Keys [lo_all, hi_all] are visible to every row of the workgroup, so tiles
+    // [full_lo, full_hi) are fully visible; a fast step needs tiles t and t+1 in that
+    // range.  Steps before it (the band's left edge) and after it (the diagonal, the
+    // band's right edge, the ragged tail) take the general path.
+    const int lo_all = WINDOW ? max(0, q_last - wl) : 0;
+    const int hi_all = min(N - 1, q0 + wr);
+    const int full_lo = (lo_all + C::BC - 1) / C::BC;
+    const int full_hi = (hi_all + 1) / C::BC;
+    const int lead_end = WINDOW ? min(max(t_begin, full_lo), ntiles) : t_begin;
+    const int nfast = max(lead_end, min(full_hi, ntiles) - 1);
+    int t = t_begin;
+    if constexpr (WINDOW) {
+        for (; t + 1 < lead_end; t += 2) {
+            step(t, sa, sb);
+            step(t + 1, sb, sa);
+        }
+        if (t < lead_end) {
+            step(t, sa, sb);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
+            ++t;
+        }
+    }
     for (; t + 1 < nfast; t += 2) {
         fast_step(t, sa, sb);
         fast_step(t + 1, sb, sa);
@@ -276,7 +303,12 @@ template <int D>
 static hipError_t launch_bf16(const FwdParams& p, hipStream_t stream) {
     constexpr int br = FwdCfg<D>::BR;
     const long long nblk = (long long)p.B * p.Hq * ((p.N + br - 1) / br);
-    hipLaunchKernelGGL((fa_fwd_bf16_kernel<D>), dim3((unsigned)nblk), dim3(FwdCfg<D>::THREADS), 0, stream, p);
+    if (p.window >= 0)
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, true>), dim3((unsigned)nblk), dim3(FwdCfg<D>::THREADS), 0, stream,
+                           p);
+    else
+        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, false>), dim3((unsigned)nblk), dim3(FwdCfg<D>::THREADS), 0, stream,
+                           p);
     return hipGetLastError();
 }
 

@@ -45,15 +45,16 @@ __device__ __forceinline__ float pair_max(float x) {
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Keys >= N, and with `causal` keys after the query's position `q` (this lane's
-// column): masked scores become -inf (p = 0).
-__device__ __forceinline__ void fwd_mask(f32x16 (&s)[2], int k0, int q, int N, int causal, int hh) {
+// Keys outside [lo, hi], this lane's visible band (hi already clipped below N; lo
+// checked only when LO): masked scores become -inf (p = 0).
+template <bool LO>
+__device__ __forceinline__ void fwd_mask(f32x16 (&s)[2], int k0, int lo, int hi, int hh) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool vis = key < N && (!causal || key <= q);
+            const bool vis = key <= hi && (!LO || key >= lo);
             s[kb][r] = vis ? s[kb][r] : kNegInf;
         }
 }

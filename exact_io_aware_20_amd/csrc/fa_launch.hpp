@@ -12,6 +12,7 @@ struct FwdParams {
     void* o;
     float* lse;
     int B, Hq, Hkv, N, causal;
+    int window;         // sliding window: key j visible to query i only if |i - j| <= window; < 0: none
     float scale;        // softmax scale
     float scale_log2;   // scale * log2(e)
 };
@@ -29,6 +30,7 @@ struct BwdParams {
     float* dsum;        // workspace: D_i = dO_i . O_i, one fp32 per query row
     float* lse2;        // workspace: LSE_i * log2(e), one fp32 per query row
     int B, Hq, Hkv, N, causal;
+    int window;         // as in FwdParams
     float scale;
     float scale_log2;
 };

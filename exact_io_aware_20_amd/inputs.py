@@ -16,13 +16,16 @@ gqa_n4096_d128                8    24    2   4096  128  yes     bf16   fwd, bwd
 longctx_n65536_d128           1    16   16  65536  128  both    bf16   fwd
 decode_gqa_kv65536_d128       8    24    2  65536  128  yes     bf16   decode, Nq=1
 decode_spec4_kv65536_d128     8    24    2  65536  128  yes     bf16   decode, Nq=4
+window_n16384_w2047_d128      2    16   16  16384  128  yes     bf16   fwd, bwd (window 2047)
 ==========================  ====  ===  ===  =====  ===  ======  =====  ===========
 
 The long-context workload multiplies q and k by 8 before the cast (a power of two,
 exact in bf16), so logits reach |x| ~ 500 and stress the running-max rescaling.
 The decode workloads hold a cache of N = 65536 keys and values per KV head and
 Nq = 1 (one new token) or Nq = 4 (four tokens checked at once) queries per query
-head; q is [B, Hq, Nq, d] and k, v are [B, Hkv, N, d].
+head; q is [B, Hq, Nq, d] and k, v are [B, Hkv, N, d].  The window workload lets each
+query see only keys within 2047 positions (with the causal rule: its 2048 most recent
+tokens, itself included).
 """
 from __future__ import annotations
 
@@ -47,6 +50,7 @@ class Workload:
     qk_mult: float = 1.0
     extra: dict = field(default_factory=dict)
     nq: int = 0            # decode: query rows per head (0: the queries are the whole sequence)
+    window: int = -1       # sliding window |i - j| <= window (-1: none)
 
     @property
     def decode(self) -> bool:
@@ -71,6 +75,7 @@ WORKLOADS = {
                  False, qk_mult=8.0),
         Workload("decode_gqa_kv65536_d128", 6000, 8, 24, 2, 65536, 128, (True,), "bf16", False, nq=1),
         Workload("decode_spec4_kv65536_d128", 7000, 8, 24, 2, 65536, 128, (True,), "bf16", False, nq=4),
+        Workload("window_n16384_w2047_d128", 8000, 2, 16, 16, 16384, 128, (True,), "bf16", True, window=2047),
     )
 }
 

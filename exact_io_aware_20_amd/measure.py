@@ -76,3 +76,20 @@ def decode_flops(B, Hq, Nq, Nk, d) -> float:
     """Two Nq x Nk x d contractions per query head (the causal mask hides at most
     Nq - 1 keys of Nk, so the full count is used)."""
     return 4.0 * B * Hq * Nq * Nk * d
+
+
+def visible_pairs(N, causal: bool, window: int = -1) -> int:
+    """Number of (query, key) pairs with key j visible to query i: j <= i when causal,
+    |i - j| <= window when window >= 0 (exact count, no halving convention)."""
+    w = N if window < 0 else window
+    total = 0
+    for i in range(N):
+        lo = max(0, i - w)
+        hi = i if causal else min(N - 1, i + w)
+        total += hi - lo + 1
+    return total
+
+
+def window_fwd_flops(B, Hq, N, d, causal: bool, window: int) -> float:
+    """Forward of a sliding-window call: two contractions over the visible pairs."""
+    return 4.0 * B * Hq * d * visible_pairs(N, causal, window)

@@ -59,7 +59,8 @@ typedef enum fa_status {
     FA_ERR_FLAG = 7,       /* causal is not 0 or 1                               */
     FA_ERR_WORKSPACE = 8,  /* workspace NULL, misaligned or too small            */
     FA_ERR_ALIAS = 9,      /* an output overlaps an input or another output     */
-    FA_ERR_LAUNCH = 10     /* hipGetLastError reported a launch failure          */
+    FA_ERR_LAUNCH = 10,    /* hipGetLastError reported a launch failure          */
+    FA_ERR_WINDOW = 11     /* window is negative                                 */
 } fa_status;
 
 /*
@@ -126,6 +127,34 @@ fa_status fa_backward_dq(const void* q, const void* k, const void* v, const void
                          const void* workspace, size_t workspace_bytes,
                          void* dq, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                          hipStream_t stream);
+
+/*
+ * Sliding-window attention: as fa_forward / fa_backward (and its dK/dV and dQ
+ * steps), with key j visible to query i only if |i - j| <= window, on top of the
+ * causal rule; a causal row thus sees its window + 1 most recent keys (page "ZeRO 与
+ * FlashAttention 各优化什么?", "注意力瓶颈与优化路线": a sliding window limits the
+ * positions a query sees and the work done).  window >= 0 (FA_ERR_WINDOW otherwise);
+ * a window of N - 1 or more is no restriction.  Tiles wholly outside the band are
+ * neither loaded nor computed.  Other arguments, layouts and errors are those of the
+ * calls without a window; the backward takes lse from fa_forward_window with the same
+ * window, and the dK/dV and dQ steps take the workspace of fa_backward_preprocess.
+ */
+fa_status fa_forward_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Hq, int Hkv, int N, int d, int causal, int window, float scale,
+                            hipStream_t stream);
+fa_status fa_backward_window(const void* q, const void* k, const void* v, const void* o,
+                             const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes,
+                             int B, int Hq, int Hkv, int N, int d, int causal, int window, float scale,
+                             hipStream_t stream);
+fa_status fa_backward_dkdv_window(const void* q, const void* k, const void* v, const void* dO,
+                                  const void* workspace, size_t workspace_bytes,
+                                  void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal,
+                                  int window, float scale, hipStream_t stream);
+fa_status fa_backward_dq_window(const void* q, const void* k, const void* v, const void* dO,
+                                const void* workspace, size_t workspace_bytes,
+                                void* dq, int B, int Hq, int Hkv, int N, int d, int causal,
+                                int window, float scale, hipStream_t stream);
 
 /*
  * Decode forward: Nq new queries per head against a cache of Nk keys and values.

@@ -166,3 +166,19 @@ def test_decode_steps_reject_before_launch():
         assert fn(Q, K, V, O, L, 0x60_0000_0000, need - 4, 1, 4, 2, 2, 100, 64, 1, 0.1, None) == 8
         assert fn(Q, K, V, O, O, 0x60_0000_0000, need, 1, 4, 2, 2, 100, 64, 1, 0.1, None) == 9
         assert fn(Q, K, V, O, L, 0x60_0000_0000, need, 1, 4, 2, 200, 100, 64, 1, 0.1, None) == 2
+
+
+def test_window_calls_reject_before_launch():
+    lib = api.load_library()
+    dO, ws, dq, dk, dv = 0x20_0000_0000, 0x60_0000_0000, 0x30_0000_0000, 0x40_0000_0000, 0x50_0000_0000
+    need = lib.fa_backward_workspace_bytes(1, 2, 16)
+    assert lib.fa_forward_window(Q, K, V, O, L, 1, 2, 1, 16, 64, 1, -1, 0.1, None) == 11
+    assert lib.fa_forward_window(Q, K, V, O, L, 1, 2, 1, 16, 80, 1, 4, 0.1, None) == 4
+    assert lib.fa_forward_window(Q, K, V, Q, L, 1, 2, 1, 16, 64, 1, 4, 0.1, None) == 9
+    assert lib.fa_backward_window(Q, K, V, O, dO, L, dq, dk, dv, ws, need, 1, 2, 1, 16, 64, 1, -3, 0.1, None) == 11
+    assert lib.fa_backward_window(Q, K, V, O, dO, L, dq, dk, dv, ws, need - 4, 1, 2, 1, 16, 64, 1, 3, 0.1,
+                                  None) == 8
+    assert lib.fa_backward_dkdv_window(Q, K, V, dO, ws, need, dk, dv, 1, 2, 1, 16, 64, 1, -1, 0.1, None) == 11
+    assert lib.fa_backward_dkdv_window(Q, K, V, dO, ws, need, dk, dk, 1, 2, 1, 16, 64, 1, 2, 0.1, None) == 9
+    assert lib.fa_backward_dq_window(Q, K, V, dO, ws, need, dq, 1, 2, 1, 16, 64, 1, -1, 0.1, None) == 11
+    assert lib.fa_backward_dq_window(Q, K, V, dO, ws, need, dq, 1, 3, 2, 16, 64, 1, 2, 0.1, None) == 3
