@@ -285,3 +285,36 @@ def decode_forward(q, k, v, causal: bool, scale: float, heads=None, workers: int
         o[b, h] = ob
         lse[b, h] = lb
     return o, lse
+
+
+def paged_gather(pages, block_table, seq_len: int, b: int):
+    """The first ``seq_len`` tokens of sequence b from a paged pool, contiguous.
+
+    pages [num_pages, Hkv, P, d]: page p holds P consecutive tokens of every KV head;
+    block_table[b, i] is the page holding the sequence's tokens i*P .. i*P + P - 1
+    (lecture summary, "衡量并优化推理": metadata maps logical token positions to
+    physical blocks).  Returns [Hkv, seq_len, d].
+    """
+    pages = _f64(pages)
+    table = np.asarray(block_table, dtype=np.int64)
+    psize = pages.shape[2]
+    tok = np.arange(seq_len)
+    phys = table[b, tok // psize]
+    return np.transpose(pages[phys, :, tok % psize, :], (1, 0, 2))
+
+
+def paged_decode_forward(q, k_pages, v_pages, block_table, seq_lens, causal: bool, scale: float,
+                         workers: int = 1):
+    """Decode against a paged key/value cache: sequence b's Nk_b = seq_lens[b] cached
+    tokens are gathered through the block table, then attended exactly as
+    ``decode_forward`` (its Nq queries at positions Nk_b - Nq + i).  q [B,Hq,Nq,d].
+    Returns O [B,Hq,Nq,d] and LSE [B,Hq,Nq] (float64)."""
+    q = _f64(q)
+    o = np.full(q.shape, np.nan)
+    lse = np.full(q.shape[:3], np.nan)
+    for b in range(q.shape[0]):
+        n = int(seq_lens[b])
+        kb = paged_gather(k_pages, block_table, n, b)[None]
+        vb = paged_gather(v_pages, block_table, n, b)[None]
+        o[b:b + 1], lse[b:b + 1] = decode_forward(q[b:b + 1], kb, vb, causal, scale, workers=workers)
+    return o, lse
