@@ -23,6 +23,7 @@ ENTRY_POINTS = ("fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_work
                 "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq",
                 "fa_decode_forward", "fa_decode_workspace_bytes", "fa_decode_split", "fa_decode_merge",
                 "fa_forward_window", "fa_backward_window", "fa_backward_dkdv_window", "fa_backward_dq_window",
+                "fa_decode_paged_forward", "fa_decode_paged_split", "fa_decode_paged_merge",
                 "fa_check_args", "fa_status_string")
 
 _lib = None
@@ -72,6 +73,9 @@ def load_library() -> ctypes.CDLL:
     lib.fa_backward_dkdv_window.restype = i
     lib.fa_backward_dq_window.argtypes = [vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, i, i, f, vp]
     lib.fa_backward_dq_window.restype = i
+    for fn in (lib.fa_decode_paged_forward, lib.fa_decode_paged_split, lib.fa_decode_paged_merge):
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, i, i, i, f, vp]
+        fn.restype = i
     lib.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i]
     lib.fa_check_args.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -168,6 +172,38 @@ def decode_forward(q, k, v, causal: bool, scale: float, o=None, lse=None, worksp
     code = getattr(lib, fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                             B, Hq, Hkv, Nq, Nk, d, int(causal), float(scale), _stream(stream))
+    _check(fn, code)
+    return o, lse
+
+
+def decode_paged_forward(q, k_pages, v_pages, block_table, seq_lens, max_seq_len: int, causal: bool, scale: float,
+                         o=None, lse=None, workspace=None, stream=None, step: str = "all"):
+    """bf16 decode against a paged cache via fa_decode_paged_forward (or its split /
+    merge kernel alone).  q [B,Hq,Nq,d]; k_pages, v_pages [num_pages,Hkv,page_size,d];
+    block_table int32 [B,max_blocks]; seq_lens int32 [B].  Returns (o, lse)."""
+    fn = {"all": "fa_decode_paged_forward", "split": "fa_decode_paged_split", "merge": "fa_decode_paged_merge"}[step]
+    lib = load_library()
+    if q.dim() != 4 or k_pages.dim() != 4:
+        raise ValueError("q must be [B, Hq, Nq, d] and the pools [num_pages, Hkv, page_size, d]")
+    B, Hq, Nq, d = q.shape
+    num_pages, Hkv, page_size = k_pages.shape[:3]
+    max_blocks = block_table.shape[1]
+    _require(q, "q", torch.bfloat16, (B, Hq, Nq, d))
+    _require(k_pages, "k_pages", torch.bfloat16, (num_pages, Hkv, page_size, d))
+    _require(v_pages, "v_pages", torch.bfloat16, (num_pages, Hkv, page_size, d))
+    _require(block_table, "block_table", torch.int32, (B, max_blocks))
+    _require(seq_lens, "seq_lens", torch.int32, (B,))
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _require(o, "o", torch.bfloat16, (B, Hq, Nq, d))
+    _require(lse, "lse", torch.float32, (B, Hq, Nq))
+    if workspace is None:
+        nbytes = decode_workspace_bytes(B, Hq, Hkv, Nq, max_seq_len, d)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    code = getattr(lib, fn)(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+                            seq_lens.data_ptr(), o.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), B, Hq, Hkv, Nq, int(max_seq_len),
+                            num_pages, page_size, max_blocks, d, int(causal), float(scale), _stream(stream))
     _check(fn, code)
     return o, lse
 

@@ -212,6 +212,47 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d) 
     return fa::decode_plan(B, Hq, Hkv, Nq, Nk, d).workspace_bytes;
 }
 
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+fa_status check_paged(const void* q, const void* kp, const void* vp, const int* table, const int* seq_lens,
+                      const void* o, const void* lse, const void* workspace, size_t ws_bytes, int B, int Hq, int Hkv,
+                      int Nq, int max_seq_len, int num_pages, int page_size, int max_blocks, int d, int causal,
+                      float scale) {
+    if (!q || !kp || !vp || !table || !seq_lens || !o || !lse) return FA_ERR_NULL;
+    fa_status s = check_decode_shape(B, Hq, Hkv, Nq, max_seq_len, d, causal, scale);
+    if (s != FA_OK) return s;
+    if (page_size < 64 || page_size % 64 != 0 || max_blocks < 1 || num_pages < 1 ||
+        (long long)max_blocks * page_size < max_seq_len)
+        return FA_ERR_SHAPE;
+    const size_t ws_need = fa::decode_plan(B, Hq, Hkv, Nq, max_seq_len, d).workspace_bytes;
+    if (!workspace || !aligned16(workspace) || ws_bytes < ws_need) return FA_ERR_WORKSPACE;
+    if (!aligned4(table) || !aligned4(seq_lens)) return FA_ERR_ALIGN;
+    const uintptr_t qb = (uintptr_t)B * Hq * Nq * d * 2;
+    const uintptr_t pb = (uintptr_t)num_pages * Hkv * page_size * d * 2;
+    const Arg a[8] = {{q, qb, false},
+                      {kp, pb, false},
+                      {vp, pb, false},
+                      {table, (uintptr_t)B * max_blocks * 4, false},
+                      {seq_lens, (uintptr_t)B * 4, false},
+                      {o, qb, true},
+                      {lse, (uintptr_t)B * Hq * Nq * 4, true},
+                      {workspace, ws_need, true}};
+    // the table and lengths (entries 3, 4) need only 4-byte alignment; every entry is
+    // checked for overlap with the outputs
+    for (int i = 0; i < 8; ++i)
+        if (i != 3 && i != 4 && !aligned16(a[i].ptr)) return FA_ERR_ALIGN;
+    for (int i = 0; i < 8; ++i) {
+        if (!a[i].out) continue;
+        const uintptr_t lo = (uintptr_t)a[i].ptr, hi = lo + a[i].bytes;
+        for (int j = 0; j < 8; ++j) {
+            if (j == i) continue;
+            const uintptr_t lo2 = (uintptr_t)a[j].ptr, hi2 = lo2 + a[j].bytes;
+            if (lo < hi2 && lo2 < hi) return FA_ERR_ALIAS;
+        }
+    }
+    return FA_OK;
+}
+
 static fa_status decode_call(int steps, const void* q, const void* k, const void* v, void* o, float* lse,
                              void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk,
                              int d, int causal, float scale, hipStream_t stream) {
@@ -236,7 +277,44 @@ static fa_status decode_call(int steps, const void* q, const void* k, const void
     p.nsplit = pl.nsplit;
     p.tiles_per_split = pl.tiles_per_split;
     p.scale_log2 = kernel_scale_log2(scale);
-    return launched(fa::launch_decode(p, d, steps, stream));
+    p.block_table = nullptr;
+    p.seq_lens = nullptr;
+    p.max_blocks = p.page_size = p.num_pages = 0;
+    return launched(fa::launch_decode(p, d, steps, false, stream));
+}
+
+static fa_status paged_call(int steps, const void* q, const void* kp, const void* vp, const int* table,
+                            const int* seq_lens, void* o, float* lse, void* workspace, size_t workspace_bytes, int B,
+                            int Hq, int Hkv, int Nq, int max_seq_len, int num_pages, int page_size, int max_blocks,
+                            int d, int causal, float scale, hipStream_t stream) {
+    fa_status s = check_paged(q, kp, vp, table, seq_lens, o, lse, workspace, workspace_bytes, B, Hq, Hkv, Nq,
+                              max_seq_len, num_pages, page_size, max_blocks, d, causal, scale);
+    if (s != FA_OK) return s;
+    const fa::DecodePlan pl = fa::decode_plan(B, Hq, Hkv, Nq, max_seq_len, d);
+    fa::DecodeParams p;
+    p.q = q;
+    p.k = kp;
+    p.v = vp;
+    p.o = o;
+    p.lse = lse;
+    p.part_o = (float*)workspace;
+    p.part_lse = (float*)workspace + (size_t)pl.nsplit * B * Hq * Nq * d;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.Nq = Nq;
+    p.Nk = max_seq_len;
+    p.causal = causal;
+    p.block_table = table;
+    p.seq_lens = seq_lens;
+    p.max_blocks = max_blocks;
+    p.page_size = page_size;
+    p.num_pages = num_pages;
+    p.nrb = pl.nrb;
+    p.nsplit = pl.nsplit;
+    p.tiles_per_split = pl.tiles_per_split;
+    p.scale_log2 = kernel_scale_log2(scale);
+    return launched(fa::launch_decode(p, d, steps, true, stream));
 }
 
 fa_status fa_decode_forward(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
@@ -259,6 +337,20 @@ fa_status fa_decode_merge(const void* q, const void* k, const void* v, void* o, 
     return decode_call(fa::kDecodeMerge, q, k, v, o, lse, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, d,
                        causal, scale, stream);
 }
+
+#define FA_PAGED_ARGS                                                                                           \
+    const void *q, const void *k_pages, const void *v_pages, const int *block_table, const int *seq_lens, void *o, \
+        float *lse, void *workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int max_seq_len,     \
+        int num_pages, int page_size, int max_blocks, int d, int causal, float scale, hipStream_t stream
+#define FA_PAGED_PASS                                                                                          \
+    q, k_pages, v_pages, block_table, seq_lens, o, lse, workspace, workspace_bytes, B, Hq, Hkv, Nq, max_seq_len, \
+        num_pages, page_size, max_blocks, d, causal, scale, stream
+
+fa_status fa_decode_paged_forward(FA_PAGED_ARGS) {
+    return paged_call(fa::kDecodeSplit | fa::kDecodeMerge, FA_PAGED_PASS);
+}
+fa_status fa_decode_paged_split(FA_PAGED_ARGS) { return paged_call(fa::kDecodeSplit, FA_PAGED_PASS); }
+fa_status fa_decode_paged_merge(FA_PAGED_ARGS) { return paged_call(fa::kDecodeMerge, FA_PAGED_PASS); }
 
 size_t fa_backward_workspace_bytes(int B, int Hq, int N) { return workspace_bytes(B, Hq, N); }
 

@@ -34,7 +34,11 @@
 namespace fa {
 
 constexpr int kDecodeTile = 64;           // keys per K/V tile
-constexpr int kDecodeTargetWgs = 1024;    // one single-wave workgroup per SIMD: four per CU on 256 CUs
+// One single-wave workgroup per SIMD: four per CU on 256 CUs.  Paged calls plan for
+// their longest sequence (the only length the host knows), so with mixed lengths the
+// splits past a shorter sequence's end exit at once; planning more, shorter splits
+// (2048 to 4096), or issuing splits before sequences, measured slower.
+constexpr int kDecodeTargetWgs = 1024;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8); the counters not named are left at their maximum.
@@ -54,7 +58,7 @@ __device__ __forceinline__ void decode_mask(f32x16 (&s)[2], int kb, int klo, int
         }
 }
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_decode_split_kernel(DecodeParams p) {
     using S = SwzTile<D, 1>;
@@ -79,7 +83,9 @@ void fa_decode_split_kernel(DecodeParams p) {
     const int b = bh / p.Hkv;
     const int hkv = bh - b * p.Hkv;
     const int G = p.Hq / p.Hkv;
-    const int Nq = p.Nq, Nk = p.Nk;
+    const int Nq = p.Nq;
+    // this sequence's cached tokens (paged: its own length, at most the planned Nk)
+    const int Nk = PAGED ? min(max(p.seq_lens[b], 0), p.Nk) : p.Nk;
 
     // this lane's query column: packed row r = (head within the group) * Nq + query
     const int r = rb * 32 + l32;
@@ -89,8 +95,8 @@ void fa_decode_split_kernel(DecodeParams p) {
     const size_t qrow = ((size_t)b * p.Hq + (size_t)hkv * G + hl) * Nq + qi;
     const int pos = live ? Nk - Nq + qi : Nk - 1;   // position in the key sequence
 
-    const uint16_t* Kh = (const uint16_t*)p.k + (size_t)bh * Nk * D;
-    const uint16_t* Vh = (const uint16_t*)p.v + (size_t)bh * Nk * D;
+    const uint16_t* Kp = (const uint16_t*)p.k;
+    const uint16_t* Vp = (const uint16_t*)p.v;
     const uint16_t* Qr = (const uint16_t*)p.q + qrow * D;
 
     u32x4 qf[D / 16];
@@ -106,11 +112,30 @@ void fa_decode_split_kernel(DecodeParams p) {
     const int ntiles = (Nk + kDecodeTile - 1) / kDecodeTile;
     const int t0 = split * p.tiles_per_split;
     const int t1 = min(ntiles, t0 + p.tiles_per_split);
-    // Tile t holds the 64 keys starting at kbase(t).  A ragged last tile is read as
-    // the last 64 keys of the cache, its keys below 64 t (already in tile t-1)
-    // masked, so that every load inside the loop is a whole tile; only a cache
-    // shorter than one tile (a single tile, loaded before the loop) clamps its rows.
-    auto kbase = [&](int t) { return Nk >= kDecodeTile ? min(t * kDecodeTile, Nk - kDecodeTile) : 0; };
+    // Tile t holds the 64 keys starting at kbase(t), read from element offset
+    // tile_off(t) of the K and V arrays.  Contiguous cache: a ragged last tile is read
+    // as the last 64 keys of the cache, its keys below 64 t (already in tile t-1)
+    // masked, so that every load inside the loop is a whole tile; only a cache shorter
+    // than one tile (a single tile, loaded before the loop) clamps its rows.  Paged
+    // cache: a tile lies inside one page (page_size is a multiple of 64) and pages are
+    // whole allocations, so every tile is read whole and keys >= Nk are masked; a
+    // table entry outside [0, num_pages) is read as page 0 and its keys masked.
+    auto kbase = [&](int t) {
+        if (PAGED) return t * kDecodeTile;
+        return Nk >= kDecodeTile ? min(t * kDecodeTile, Nk - kDecodeTile) : 0;
+    };
+    auto tile_off = [&](int t, bool& bad) -> size_t {
+        if constexpr (PAGED) {
+            const int key = t * kDecodeTile;
+            int pg = p.block_table[(size_t)b * p.max_blocks + key / p.page_size];
+            bad = (unsigned)pg >= (unsigned)p.num_pages;
+            pg = bad ? 0 : pg;
+            return (((size_t)pg * p.Hkv + hkv) * p.page_size + key % p.page_size) * D;
+        } else {
+            bad = false;
+            return ((size_t)bh * Nk + kbase(t)) * D;
+        }
+    };
     // keys at or after this index may be invisible to some column of the block
     const int mask_from = p.causal ? Nk - Nq + 1 : Nk;
 
@@ -120,23 +145,28 @@ void fa_decode_split_kernel(DecodeParams p) {
     // One tile in flight per operand: K(t+1) is fetched while tile t's softmax and
     // P.V run, V(t+1) while S(t+1) runs.  Loads retire in order, so "at most
     // Dma::PER outstanding" means the older of the two tiles in flight has landed.
+    bool bad = false;
+    size_t off = 0;
     if (t0 < t1) {
-        const int kb0 = kbase(t0);
-        dma.issue(Kh + (size_t)kb0 * D, Nk - kb0, kbuf, 0);
-        dma.issue(Vh + (size_t)kb0 * D, Nk - kb0, vbuf, 0);
+        off = tile_off(t0, bad);
+        const int nvalid = PAGED ? kDecodeTile : Nk - kbase(t0);
+        dma.issue(Kp + off, nvalid, kbuf, 0);
+        dma.issue(Vp + off, nvalid, vbuf, 0);
     }
     for (int t = t0; t < t1; ++t) {
         const int klo = t * kDecodeTile;
         const int kb = kbase(t);
         const bool more = t + 1 < t1;
-        const int kb1 = kbase(t + 1);
+        bool bad1 = false;
+        const size_t off1 = more ? tile_off(t + 1, bad1) : 0;
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(Dma::PER));   // K(t) has landed
         f32x16 s[2];
         fwd_scores<D, 1>(kbuf, qf, s, l32, hh);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);              // K(t) fully read
-        if (more) dma.issue_full(Kh + (size_t)kb1 * D, kbuf, 0);
-        if (kb < klo || kb + kDecodeTile > mask_from) decode_mask(s, kb, klo, pos, Nk, p.causal, hh);
+        if (more) dma.issue_full(Kp + off1, kbuf, 0);
+        if (kb < klo || kb + kDecodeTile > mask_from || bad)
+            decode_mask(s, kb, klo, pos, bad ? kb : Nk, p.causal, hh);
         fwd_rescale<D>(s, o, m_ref, l_part, sl2);
         u32x4 pf[2][2];
         fwd_probs(s, m_ref, sl2, pf, l_part);
@@ -147,7 +177,9 @@ void fa_decode_split_kernel(DecodeParams p) {
         fwd_pv<D>(vbuf, pf, o, lane);
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);              // V(t) fully read
-        if (more) dma.issue_full(Vh + (size_t)kb1 * D, vbuf, 0);
+        if (more) dma.issue_full(Vp + off1, vbuf, 0);
+        off = off1;
+        bad = bad1;
     }
 
     // ---- epilogue: l over the lane pair; a column that saw no key (possible only
@@ -205,7 +237,16 @@ __global__ __launch_bounds__(256) void fa_decode_merge_kernel(DecodeParams p) {
     for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     if (lane == 0) mred[wave] = mx;
     __syncthreads();
-    const float M = fmaxf(fmaxf(mred[0], mred[1]), fmaxf(mred[2], mred[3]));   // finite: each row sees a key
+    const float M = fmaxf(fmaxf(mred[0], mred[1]), fmaxf(mred[2], mred[3]));
+    if (M == kNegInf) {   // no split saw a key (a paged sequence shorter than its queries)
+        if (wave == 0) {
+            uint16_t* Or = (uint16_t*)p.o + row * D + lane * E;
+#pragma unroll
+            for (int e = 0; e < E; ++e) Or[e] = 0;
+            if (lane == 0) p.lse[row] = kNegInf;
+        }
+        return;
+    }
 
     float acc[E];
 #pragma unroll
@@ -249,11 +290,12 @@ __global__ __launch_bounds__(256) void fa_decode_merge_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------------
 DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
     DecodePlan pl{};
+    const long long target = kDecodeTargetWgs;
     const long long G = Hq / Hkv;
     const long long ntiles = (Nk + kDecodeTile - 1) / kDecodeTile;
     pl.nrb = (int)((G * Nq + 31) / 32);
     const long long units = (long long)B * Hkv * pl.nrb;   // workgroups per split
-    long long per = (ntiles * units + kDecodeTargetWgs - 1) / kDecodeTargetWgs;
+    long long per = (ntiles * units + target - 1) / target;
     per = per < 1 ? 1 : (per > ntiles ? ntiles : per);
     pl.tiles_per_split = (int)per;
     pl.nsplit = (int)((ntiles + per - 1) / per);
@@ -263,10 +305,13 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
 }
 
 template <int D>
-static hipError_t launch_decode_d(const DecodeParams& p, int steps, hipStream_t stream) {
+static hipError_t launch_decode_d(const DecodeParams& p, int steps, bool paged, hipStream_t stream) {
     if (steps & kDecodeSplit) {
         const long long grid = (long long)p.B * p.Hkv * p.nrb * p.nsplit;
-        hipLaunchKernelGGL((fa_decode_split_kernel<D>), dim3((unsigned)grid), dim3(64), 0, stream, p);
+        if (paged)
+            hipLaunchKernelGGL((fa_decode_split_kernel<D, true>), dim3((unsigned)grid), dim3(64), 0, stream, p);
+        else
+            hipLaunchKernelGGL((fa_decode_split_kernel<D, false>), dim3((unsigned)grid), dim3(64), 0, stream, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -278,8 +323,8 @@ static hipError_t launch_decode_d(const DecodeParams& p, int steps, hipStream_t 
     return hipSuccess;
 }
 
-hipError_t launch_decode(const DecodeParams& p, int d, int steps, hipStream_t stream) {
-    return d == 64 ? launch_decode_d<64>(p, steps, stream) : launch_decode_d<128>(p, steps, stream);
+hipError_t launch_decode(const DecodeParams& p, int d, int steps, bool paged, hipStream_t stream) {
+    return d == 64 ? launch_decode_d<64>(p, steps, paged, stream) : launch_decode_d<128>(p, steps, paged, stream);
 }
 
 }  // namespace fa

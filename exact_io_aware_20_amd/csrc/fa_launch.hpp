@@ -46,7 +46,12 @@ struct DecodeParams {
     float* lse;
     float* part_o;      // workspace: fp32 [nsplit][B*Hq*Nq][d], each split's normalised O
     float* part_lse;    // workspace: fp32 [nsplit][B*Hq*Nq], each split's LSE in base 2
-    int B, Hq, Hkv, Nq, Nk, causal;
+    int B, Hq, Hkv, Nq, Nk, causal;   // paged: Nk is the longest sequence the plan covers
+    // paged cache (k, v are pools [num_pages][Hkv][page_size][d]): sequence b's token t
+    // is row t % page_size of page block_table[b * max_blocks + t / page_size]
+    const int* block_table;
+    const int* seq_lens;  // [B] tokens of each sequence
+    int max_blocks, page_size, num_pages;
     int nrb;            // 32-row blocks of the G*Nq packed query rows of a KV head
     int nsplit, tiles_per_split;
     float scale_log2;
@@ -66,7 +71,7 @@ long long bwd_grid_max(int B, int Hq, int Hkv, int N, int d);
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t stream);
 enum DecodeSteps { kDecodeSplit = 1, kDecodeMerge = 2 };
-hipError_t launch_decode(const DecodeParams& p, int d, int steps, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int d, int steps, bool paged, hipStream_t stream);
 hipError_t launch_bwd_pre(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t stream);

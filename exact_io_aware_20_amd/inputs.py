@@ -17,6 +17,7 @@ longctx_n65536_d128           1    16   16  65536  128  both    bf16   fwd
 decode_gqa_kv65536_d128       8    24    2  65536  128  yes     bf16   decode, Nq=1
 decode_spec4_kv65536_d128     8    24    2  65536  128  yes     bf16   decode, Nq=4
 window_n16384_w2047_d128      2    16   16  16384  128  yes     bf16   fwd, bwd (window 2047)
+decode_paged_kv65536_d128    16    24    2  65536  128  yes     bf16   paged decode, Nq=1
 ==========================  ====  ===  ===  =====  ===  ======  =====  ===========
 
 The long-context workload multiplies q and k by 8 before the cast (a power of two,
@@ -25,7 +26,9 @@ The decode workloads hold a cache of N = 65536 keys and values per KV head and
 Nq = 1 (one new token) or Nq = 4 (four tokens checked at once) queries per query
 head; q is [B, Hq, Nq, d] and k, v are [B, Hkv, N, d].  The window workload lets each
 query see only keys within 2047 positions (with the causal rule: its 2048 most recent
-tokens, itself included).
+tokens, itself included).  The paged decode workload holds 16 sequences of seeded
+lengths between 2048 and 65536 tokens (the first exactly 65536) in 256-token pages
+scattered over a pool by a seeded permutation; unused table entries are -1.
 """
 from __future__ import annotations
 
@@ -51,6 +54,7 @@ class Workload:
     extra: dict = field(default_factory=dict)
     nq: int = 0            # decode: query rows per head (0: the queries are the whole sequence)
     window: int = -1       # sliding window |i - j| <= window (-1: none)
+    page_size: int = 0     # paged decode: tokens per page (0: contiguous cache); N is the longest sequence
 
     @property
     def decode(self) -> bool:
@@ -76,6 +80,8 @@ WORKLOADS = {
         Workload("decode_gqa_kv65536_d128", 6000, 8, 24, 2, 65536, 128, (True,), "bf16", False, nq=1),
         Workload("decode_spec4_kv65536_d128", 7000, 8, 24, 2, 65536, 128, (True,), "bf16", False, nq=4),
         Workload("window_n16384_w2047_d128", 8000, 2, 16, 16, 16384, 128, (True,), "bf16", True, window=2047),
+        Workload("decode_paged_kv65536_d128", 9000, 16, 24, 2, 65536, 128, (True,), "bf16", False, nq=1,
+                 page_size=256),
     )
 }
 
@@ -108,3 +114,38 @@ def make_inputs(B, Hq, Hkv, N, d, seed_base: int, dtype=torch.bfloat16, qk_mult:
 def workload_inputs(w: Workload, with_do: bool | None = None) -> dict:
     return make_inputs(w.B, w.Hq, w.Hkv, w.N, w.d, w.seed_base, w.torch_dtype, w.qk_mult,
                        w.backward if with_do is None else with_do, w.nq)
+
+
+def paged_cache(B, Hq, Hkv, Nq, max_len, d, page_size, seed_base: int, min_len: int = 1, lens=None,
+                spare_pages: int = 0, dtype=torch.bfloat16) -> dict:
+    """A paged decode call on the CPU: q [B,Hq,Nq,d]; pools k_pages, v_pages
+    [num_pages,Hkv,page_size,d]; block_table int32 [B, ceil(max_len/page_size)] with -1
+    in unused entries; seq_lens int32 [B].  Lengths are drawn from [min_len, max_len]
+    (the first is max_len) unless given; each sequence's pages are placed in the pool
+    by a seeded permutation."""
+    import numpy as np
+    rng = np.random.default_rng(seed_base + 5)
+    if lens is None:
+        lens = rng.integers(min_len, max_len + 1, size=B)
+        lens[0] = max_len
+    lens = np.asarray(lens, dtype=np.int64)
+    max_blocks = (max_len + page_size - 1) // page_size
+    need = (lens + page_size - 1) // page_size
+    num_pages = max(1, int(need.sum()) + spare_pages)
+    perm = rng.permutation(num_pages)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    nxt = 0
+    for b in range(B):
+        table[b, :need[b]] = perm[nxt:nxt + need[b]]
+        nxt += int(need[b])
+    return {
+        "q": seeded_normal((B, Hq, Nq, d), seed_base + 1, dtype),
+        "k_pages": seeded_normal((num_pages, Hkv, page_size, d), seed_base + 2, dtype),
+        "v_pages": seeded_normal((num_pages, Hkv, page_size, d), seed_base + 3, dtype),
+        "block_table": torch.from_numpy(table),
+        "seq_lens": torch.from_numpy(lens.astype(np.int32)),
+    }
+
+
+def paged_workload_inputs(w: Workload) -> dict:
+    return paged_cache(w.B, w.Hq, w.Hkv, w.nq, w.N, w.d, w.page_size, w.seed_base, min_len=2048)

@@ -93,3 +93,16 @@ def visible_pairs(N, causal: bool, window: int = -1) -> int:
 def window_fwd_flops(B, Hq, N, d, causal: bool, window: int) -> float:
     """Forward of a sliding-window call: two contractions over the visible pairs."""
     return 4.0 * B * Hq * d * visible_pairs(N, causal, window)
+
+
+def paged_decode_bytes(seq_lens, B, Hq, Hkv, Nq, d, elt: int, max_blocks: int) -> int:
+    """Paged decode call: every cached token of every sequence (K and V of each KV
+    head) read once, Q read and O, LSE written once, the block table and lengths read."""
+    tokens = int(sum(int(n) for n in seq_lens))
+    return elt * (2 * B * Hq * Nq * d + 2 * Hkv * tokens * d) + 4 * B * Hq * Nq + 4 * B * (max_blocks + 1)
+
+
+def paged_split_bytes(seq_lens, B, Hq, Hkv, Nq, d, elt: int) -> int:
+    """The paged split kernel's algorithmic traffic: Q and the cached K/V read once."""
+    tokens = int(sum(int(n) for n in seq_lens))
+    return elt * (B * Hq * Nq * d + 2 * Hkv * tokens * d)

@@ -181,8 +181,9 @@ fa_status fa_decode_forward(const void* q, const void* k, const void* v, void* o
                             int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                             hipStream_t stream);
 
-/* Bytes of device workspace fa_decode_forward needs for these sizes (it depends on
- * the sizes only); 0 for invalid sizes. */
+/* Bytes of device workspace fa_decode_forward (and fa_decode_paged_forward, with Nk
+ * its max_seq_len) needs for these sizes (it depends on the sizes only); 0 for
+ * invalid sizes. */
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 
 /*
@@ -201,6 +202,47 @@ fa_status fa_decode_merge(const void* q, const void* k, const void* v, void* o, 
                           void* workspace, size_t workspace_bytes,
                           int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                           hipStream_t stream);
+
+/*
+ * Decode forward against a paged key/value cache (Stanford lecture summary,
+ * "衡量并优化推理": the cache is cut into fixed-size blocks and metadata maps a
+ * sequence's logical token positions to physical blocks, so that memory is taken per
+ * block rather than reserved for the longest possible sequence).
+ *   k_pages, v_pages: bf16 pools [num_pages, Hkv, page_size, d]; page p holds
+ *     page_size consecutive tokens of every KV head.
+ *   block_table: int32 [B, max_blocks] (device); token t of sequence b is row
+ *     t % page_size of page block_table[b*max_blocks + t/page_size].
+ *   seq_lens: int32 [B] (device); sequence b has seq_lens[b] cached tokens, its Nq
+ *     queries sit at positions seq_lens[b] - Nq + i (as in fa_decode_forward).
+ *   max_seq_len: an upper bound of every seq_lens[b], known on the host: the key
+ *     splits and the workspace (fa_decode_workspace_bytes(B, Hq, Hkv, Nq,
+ *     max_seq_len, d)) are sized from it; larger lengths are cut to it.
+ *   q, o [B,Hq,Nq,d] bf16; lse [B,Hq,Nq] fp32.  page_size must be a multiple of
+ *   64 and max_blocks*page_size >= max_seq_len (FA_ERR_SHAPE otherwise);
+ *   block_table and seq_lens need 4-byte alignment, the rest 16 bytes.
+ * Tables are read on the device: a table entry outside [0, num_pages) contributes
+ * no keys (it is never dereferenced), and a query with no visible key (a sequence
+ * shorter than its queries under the causal rule) gets O = 0 and LSE = -inf.
+ * fa_decode_paged_split / _merge are its two kernels, as for fa_decode_forward.
+ */
+fa_status fa_decode_paged_forward(const void* q, const void* k_pages, const void* v_pages,
+                                  const int* block_table, const int* seq_lens, void* o, float* lse,
+                                  void* workspace, size_t workspace_bytes,
+                                  int B, int Hq, int Hkv, int Nq, int max_seq_len, int num_pages,
+                                  int page_size, int max_blocks, int d, int causal, float scale,
+                                  hipStream_t stream);
+fa_status fa_decode_paged_split(const void* q, const void* k_pages, const void* v_pages,
+                                const int* block_table, const int* seq_lens, void* o, float* lse,
+                                void* workspace, size_t workspace_bytes,
+                                int B, int Hq, int Hkv, int Nq, int max_seq_len, int num_pages,
+                                int page_size, int max_blocks, int d, int causal, float scale,
+                                hipStream_t stream);
+fa_status fa_decode_paged_merge(const void* q, const void* k_pages, const void* v_pages,
+                                const int* block_table, const int* seq_lens, void* o, float* lse,
+                                void* workspace, size_t workspace_bytes,
+                                int B, int Hq, int Hkv, int Nq, int max_seq_len, int num_pages,
+                                int page_size, int max_blocks, int d, int causal, float scale,
+                                hipStream_t stream);
 
 /*
  * Host-only validation of a forward call, exactly as fa_forward performs it

@@ -182,3 +182,24 @@ def test_window_calls_reject_before_launch():
     assert lib.fa_backward_dkdv_window(Q, K, V, dO, ws, need, dk, dk, 1, 2, 1, 16, 64, 1, 2, 0.1, None) == 9
     assert lib.fa_backward_dq_window(Q, K, V, dO, ws, need, dq, 1, 2, 1, 16, 64, 1, -1, 0.1, None) == 11
     assert lib.fa_backward_dq_window(Q, K, V, dO, ws, need, dq, 1, 3, 2, 16, 64, 1, 2, 0.1, None) == 3
+
+
+def test_paged_decode_rejects_before_launch():
+    lib = api.load_library()
+    KP, VP, TB, SL, ws = 0x70_0000_0000, 0x71_0000_0000, 0x72_0000_0000, 0x73_0000_0000, 0x60_0000_0000
+    need = lib.fa_decode_workspace_bytes(2, 4, 2, 1, 1000, 128)
+
+    def call(q=Q, kp=KP, tb=TB, sl=SL, o=O, wsb=None, **kw):
+        a = dict(B=2, Hq=4, Hkv=2, Nq=1, L=1000, P=10, psize=128, mb=8, d=128, causal=1)
+        a.update(kw)
+        return lib.fa_decode_paged_forward(q, kp, VP, tb, sl, o, L, ws, need if wsb is None else wsb, a["B"],
+                                           a["Hq"], a["Hkv"], a["Nq"], a["L"], a["P"], a["psize"], a["mb"], a["d"],
+                                           a["causal"], 0.1, None)
+    assert call(tb=None) == 1
+    assert call(psize=100) == 2          # not a multiple of 64
+    assert call(mb=7) == 2               # 7 * 128 < 1000 tokens
+    assert call(P=0) == 2
+    assert call(tb=TB + 2) == 6          # int32 table needs 4-byte alignment
+    assert call(wsb=need - 4) == 8
+    assert call(o=KP) == 9               # o overlaps the K pool
+    assert call(Nq=1001) == 2            # causal: more queries than the longest sequence
