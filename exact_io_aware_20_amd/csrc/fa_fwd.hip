@@ -125,17 +125,27 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // Fast step: tiles t and t+1 are fully visible to every row of the workgroup
     // (so t+1 < ntiles and V(t+1) exists; K(t+2) may not, and then the last tile
     // is reloaded into the free buffer).  One branch-free block apart from the
-    // rare rescale, in a fixed phase order: scores(t+1) to the matrix cores, the
-    // exponentials of tile t, then PV(t) (the compiler's own interleave of these
-    // phases measured slower).
+    // rare rescale: scores(t+1) on the matrix cores interleaved with the
+    // exponentials of tile t in a fixed pattern, then PV(t) (the compiler's own
+    // interleave of all three phases measured slower).
     auto fast_step = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
         fwd_rescale<D>(cur, o, m_ref, l_part, sl2);
         issue_k(min(t + 2, ntiles - 1), kbuf + (t & 1) * KB);
         issue_v(t + 1, vbuf + ((t + 1) & 1) * VB);
         u32x4 pf[2][2];
         fwd_scores<D>(kbuf + ((t + 1) & 1) * KB, qf, nxt, l32, hh);
-        __builtin_amdgcn_sched_barrier(0);
         fwd_probs(cur, m_ref, sl2, pf, l_part);
+        // Interleave the two in one instruction stream: four K-fragment reads ahead,
+        // then per score MFMA (independent of tile t's softmax) four of its vector
+        // instructions and the next fragment read, so the vector work issues while
+        // the matrix pipe is busy (≈ 3 % faster than the two blocks in sequence).
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS reads
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+            if (i < D / 8 - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
         fwd_pv<D>(vbuf + (t & 1) * VB, pf, o, lane);
         __builtin_amdgcn_s_waitcnt(0);
