@@ -132,7 +132,7 @@ def committed_traffic(md_path: str, kernel: str):
 
 def _write_trace_md(rows, timed, skip, out, command):
     lines = [f"# Kernel trace: {os.path.splitext(os.path.basename(out))[0].replace('kernel_trace_', '')}", "",
-             "Command (from the repository root on the GPU box; `$R` is the repository path):", "",
+             "Command (run from the repository root; `$R` is the repository path):", "",
              f"    {command}", "",
              f"Kernel sources digest: `{source_digest()}`.  `avg` is rocprofv3's own statistic over all "
              f"launches; `timed avg` leaves out each kernel's first {skip} (warm-up) launches, the "
@@ -151,7 +151,7 @@ def _write_trace_md(rows, timed, skip, out, command):
 def _write_traffic_md(t, out, command):
     lines = [f"# HBM traffic per launch: {os.path.splitext(os.path.basename(out))[0].replace('hbm_traffic_', '')}", "",
              "Two counter runs of the same command, one with `--pmc FETCH_SIZE`, one with",
-             "`--pmc WRITE_SIZE` (from the repository root on the GPU box; `$R` is the repository path):", "",
+             "`--pmc WRITE_SIZE` (run from the repository root; `$R` is the repository path):", "",
              f"    {command}", "",
              f"Calibration: `{t['calib_kernel']}` streams {t['calib_mib']} MiB in and {t['calib_mib']} MiB out; "
              f"true bytes / counter bytes = {t['fetch_scale']:.3f} (FETCH_SIZE), {t['write_scale']:.3f} (WRITE_SIZE).",
