@@ -40,6 +40,11 @@ Readings where the pages are silent (each listed with its reason in the design n
   "注意力瓶颈与优化路线": a sliding window restricts which positions a query sees):
   query position i sees key j only if |i - j| <= window, on top of the causal rule,
   so a causal row sees its window + 1 most recent keys.  window < 0 means no window.
+* Block-sparse layout (``block_mask``, same page and section: block-sparse and
+  global + local patterns compute only part of the positions): a 0/1 matrix over
+  BLOCK x BLOCK blocks of (query, key) positions, shared by every head; query i sees
+  key j only if block_mask[i // BLOCK][j // BLOCK] is set, on top of the causal rule.
+  A row that sees no key gets O = 0 and LSE = -inf.
 * The gradients are the analytic softmax-Jacobian gradients (the pages print none):
       dP = dO V^T,  D_i = sum_j P_ij dP_ij,  dS = P * (dP - D),
       dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO,
@@ -59,6 +64,7 @@ from concurrent.futures import ProcessPoolExecutor
 import numpy as np
 
 ROW_BLOCK = 512
+BLOCK = 64   # side of a block of the block-sparse layout
 
 
 def _f64(x) -> np.ndarray:
@@ -71,7 +77,8 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def _scores(q_rows: np.ndarray, k: np.ndarray, rows: np.ndarray, causal: bool, scale: float, window: int = -1):
+def _scores(q_rows: np.ndarray, k: np.ndarray, rows: np.ndarray, causal: bool, scale: float, window: int = -1,
+            block_mask=None):
     """S for the given query rows against all keys, with the causal mask (key <= query)
     and, for window >= 0, the sliding-window mask (|query - key| <= window) applied.
 
@@ -82,6 +89,9 @@ def _scores(q_rows: np.ndarray, k: np.ndarray, rows: np.ndarray, causal: bool, s
         s = np.where(cols[None, :] <= rows[:, None], s, -np.inf)
     if window >= 0:
         s = np.where(np.abs(cols[None, :] - rows[:, None]) <= window, s, -np.inf)
+    if block_mask is not None:
+        bm = np.asarray(block_mask, dtype=bool)
+        s = np.where(bm[rows[:, None] // BLOCK, cols[None, :] // BLOCK], s, -np.inf)
     return s
 
 
@@ -90,7 +100,8 @@ def _query_offset(nq: int, nk: int) -> int:
     return nk - nq
 
 
-def head_forward(q, k, v, causal: bool, scale: float, rows=None, offset: int = 0, window: int = -1):
+def head_forward(q, k, v, causal: bool, scale: float, rows=None, offset: int = 0, window: int = -1,
+                 block_mask=None):
     """One query head: O and LSE for the selected query rows (default: all rows).
 
     q: [Nq, d]; k, v: [Nk, d] (the KV head of this query's group); query row i sits
@@ -107,7 +118,7 @@ def head_forward(q, k, v, causal: bool, scale: float, rows=None, offset: int = 0
     lse = np.full(rows.size, -np.inf)
     for b0 in range(0, rows.size, ROW_BLOCK):
         r = rows[b0:b0 + ROW_BLOCK]
-        s = _scores(q[r], k, r + offset, causal, scale, window)
+        s = _scores(q[r], k, r + offset, causal, scale, window, block_mask)
         m = s.max(axis=1)                              # pass 1: row max
         ok = np.isfinite(m)
         e = np.exp(s - np.where(ok, m, 0.0)[:, None])  # pass 2: exponentials
@@ -118,17 +129,17 @@ def head_forward(q, k, v, causal: bool, scale: float, rows=None, offset: int = 0
     return o, lse
 
 
-def head_probs(q, k, causal: bool, scale: float, window: int = -1):
+def head_probs(q, k, causal: bool, scale: float, window: int = -1, block_mask=None):
     """The full softmax matrix P [N, N] of one head (small inputs only)."""
     q, k = _f64(q), _f64(k)
     rows = np.arange(q.shape[0])
-    s = _scores(q, k, rows, causal, scale, window)
+    s = _scores(q, k, rows, causal, scale, window, block_mask)
     m = s.max(axis=1, keepdims=True)
     e = np.exp(s - m)
     return e / e.sum(axis=1, keepdims=True)
 
 
-def head_backward(q, k, v, do, causal: bool, scale: float, window: int = -1):
+def head_backward(q, k, v, do, causal: bool, scale: float, window: int = -1, block_mask=None):
     """One query head: (dQ, dK, dV) for L = sum(dO * O), float64.
 
     dK and dV are this head's contribution to its KV head; the caller sums them
@@ -141,10 +152,11 @@ def head_backward(q, k, v, do, causal: bool, scale: float, window: int = -1):
     dv = np.zeros_like(v)
     for b0 in range(0, n, ROW_BLOCK):
         r = np.arange(b0, min(n, b0 + ROW_BLOCK))
-        s = _scores(q[r], k, r, causal, scale, window)
+        s = _scores(q[r], k, r, causal, scale, window, block_mask)
         m = s.max(axis=1, keepdims=True)
-        e = np.exp(s - m)
-        p = e / e.sum(axis=1, keepdims=True)          # P, full rows
+        ok = np.isfinite(m)                           # rows that see no key have P = 0
+        e = np.exp(s - np.where(ok, m, 0.0))
+        p = e / np.where(ok, e.sum(axis=1, keepdims=True), 1.0)   # P, full rows
         dp = do[r] @ v.T                              # dP = dO V^T
         dvec = (p * dp).sum(axis=1, keepdims=True)    # D_i = sum_j P_ij dP_ij
         ds = p * (dp - dvec)                          # dS = P * (dP - D)
@@ -172,13 +184,13 @@ def _check_shapes(q, k, v):
 
 
 def _fwd_unit(args):
-    q, k, v, causal, scale, rows, offset, window = args
-    return head_forward(q, k, v, causal, scale, rows, offset, window)
+    q, k, v, causal, scale, rows, offset, window, block_mask = args
+    return head_forward(q, k, v, causal, scale, rows, offset, window, block_mask)
 
 
 def _bwd_unit(args):
-    q, k, v, do, causal, scale, window = args
-    return head_backward(q, k, v, do, causal, scale, window)
+    q, k, v, do, causal, scale, window, block_mask = args
+    return head_backward(q, k, v, do, causal, scale, window, block_mask)
 
 
 @contextlib.contextmanager
@@ -207,12 +219,14 @@ def _run(fn, jobs, workers: int):
 
 
 def attention_forward(q, k, v, causal: bool, scale: float, heads=None, rows=None, workers: int = 1,
-                      window: int = -1):
+                      window: int = -1, block_mask=None):
     """O [B,Hq,N,d] and LSE [B,Hq,N] (float64) for every (b, hq) in ``heads``.
 
     ``heads`` is an iterable of (b, hq) pairs (default: all); entries of heads not
     listed are NaN.  ``rows`` optionally restricts the computed query rows (the same
     rows for every listed head).  ``workers`` > 1 runs heads in a process pool.
+    ``window`` >= 0 adds the sliding-window mask |i - j| <= window; ``block_mask`` (a
+    0/1 matrix over BLOCK x BLOCK blocks) the block-sparse layout.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     _check_shapes(q, k, v)
@@ -221,7 +235,8 @@ def attention_forward(q, k, v, causal: bool, scale: float, heads=None, rows=None
     heads = [(b, h) for b in range(b_) for h in range(hq_)] if heads is None else list(heads)
     o = np.full(q.shape, np.nan)
     lse = np.full(q.shape[:3], np.nan)
-    jobs = [(q[b, h], k[b, _group(h, hq_, hkv_)], v[b, _group(h, hq_, hkv_)], causal, scale, rows, 0, window)
+    bm = None if block_mask is None else np.asarray(block_mask, dtype=bool)
+    jobs = [(q[b, h], k[b, _group(h, hq_, hkv_)], v[b, _group(h, hq_, hkv_)], causal, scale, rows, 0, window, bm)
             for b, h in heads]
     results = _run(_fwd_unit, jobs, workers)
     sel = slice(None) if rows is None else np.asarray(rows)
@@ -232,7 +247,7 @@ def attention_forward(q, k, v, causal: bool, scale: float, heads=None, rows=None
 
 
 def attention_backward(q, k, v, do, causal: bool, scale: float, groups=None, workers: int = 1,
-                       window: int = -1):
+                       window: int = -1, block_mask=None):
     """dQ [B,Hq,N,d], dK and dV [B,Hkv,N,d] (float64) for the listed (b, hkv) groups.
 
     A group's dK/dV is the sum over its Hq/Hkv query heads; the dQ of every query
@@ -248,7 +263,8 @@ def attention_backward(q, k, v, do, causal: bool, scale: float, groups=None, wor
     dk = np.full(k.shape, np.nan)
     dv = np.full(v.shape, np.nan)
     units = [(b, hk, h) for b, hk in groups for h in range(hk * g, hk * g + g)]
-    jobs = [(q[b, h], k[b, hk], v[b, hk], do[b, h], causal, scale, window) for b, hk, h in units]
+    bm = None if block_mask is None else np.asarray(block_mask, dtype=bool)
+    jobs = [(q[b, h], k[b, hk], v[b, hk], do[b, h], causal, scale, window, bm) for b, hk, h in units]
     results = _run(_bwd_unit, jobs, workers)
     for b, hk in groups:
         dk[b, hk] = 0.0
@@ -279,7 +295,7 @@ def decode_forward(q, k, v, causal: bool, scale: float, heads=None, workers: int
     off = _query_offset(nq, nk)
     o = np.full(q.shape, np.nan)
     lse = np.full(q.shape[:3], np.nan)
-    jobs = [(q[b, h], k[b, _group(h, hq_, hkv_)], v[b, _group(h, hq_, hkv_)], causal, scale, None, off, -1)
+    jobs = [(q[b, h], k[b, _group(h, hq_, hkv_)], v[b, _group(h, hq_, hkv_)], causal, scale, None, off, -1, None)
             for b, h in heads]
     for (b, h), (ob, lb) in zip(heads, _run(_fwd_unit, jobs, workers)):
         o[b, h] = ob

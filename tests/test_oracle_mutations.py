@@ -47,7 +47,7 @@ def test_unpatched_oracle_passes():
     assert _pins_hold()
 
 
-def _scores_no_scale(q_rows, k, rows, causal, scale, window=-1):
+def _scores_no_scale(q_rows, k, rows, causal, scale, window=-1, block_mask=None):
     s = q_rows @ k.T
     if causal:
         cols = np.arange(k.shape[0])
@@ -55,7 +55,7 @@ def _scores_no_scale(q_rows, k, rows, causal, scale, window=-1):
     return s
 
 
-def _scores_strict_mask(q_rows, k, rows, causal, scale, window=-1):
+def _scores_strict_mask(q_rows, k, rows, causal, scale, window=-1, block_mask=None):
     s = scale * (q_rows @ k.T)
     if causal:
         cols = np.arange(k.shape[0])
@@ -63,7 +63,7 @@ def _scores_strict_mask(q_rows, k, rows, causal, scale, window=-1):
     return s
 
 
-def _scores_upper_mask(q_rows, k, rows, causal, scale, window=-1):
+def _scores_upper_mask(q_rows, k, rows, causal, scale, window=-1, block_mask=None):
     s = scale * (q_rows @ k.T)
     if causal:
         cols = np.arange(k.shape[0])
@@ -71,12 +71,12 @@ def _scores_upper_mask(q_rows, k, rows, causal, scale, window=-1):
     return s
 
 
-def _bwd_wrong_sign(q, k, v, do, causal, scale, window=-1):
+def _bwd_wrong_sign(q, k, v, do, causal, scale, window=-1, block_mask=None):
     dq, dk, dv = _orig_bwd(q, k, v, do, causal, scale)
     return -dq, -dk, dv
 
 
-def _bwd_no_d_term(q, k, v, do, causal, scale, window=-1):
+def _bwd_no_d_term(q, k, v, do, causal, scale, window=-1, block_mask=None):
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     rows = np.arange(q.shape[0])
     p = A.head_probs(q, k, causal, scale)
@@ -84,7 +84,7 @@ def _bwd_no_d_term(q, k, v, do, causal, scale, window=-1):
     return scale * ds @ k, scale * ds.T @ q, p.T @ do
 
 
-def _bwd_transposed_dv(q, k, v, do, causal, scale, window=-1):
+def _bwd_transposed_dv(q, k, v, do, causal, scale, window=-1, block_mask=None):
     dq, dk, dv = _orig_bwd(q, k, v, do, causal, scale)
     p = A.head_probs(q, k, causal, scale)
     return dq, dk, p @ np.asarray(do, dtype=np.float64)   # P dO instead of P^T dO

@@ -126,7 +126,7 @@ def test_window_gradients_by_central_differences():
             assert num == pytest.approx(g[idx], rel=1e-6, abs=1e-8)
 
 
-def _scores_window_off_by_one(q_rows, k, rows, causal, scale, window=-1):
+def _scores_window_off_by_one(q_rows, k, rows, causal, scale, window=-1, block_mask=None):
     s = scale * (q_rows @ k.T)
     cols = np.arange(k.shape[0])
     if causal:
@@ -136,7 +136,7 @@ def _scores_window_off_by_one(q_rows, k, rows, causal, scale, window=-1):
     return s
 
 
-def _scores_window_one_sided(q_rows, k, rows, causal, scale, window=-1):
+def _scores_window_one_sided(q_rows, k, rows, causal, scale, window=-1, block_mask=None):
     s = scale * (q_rows @ k.T)
     cols = np.arange(k.shape[0])
     if causal:
