@@ -24,6 +24,8 @@ ENTRY_POINTS = ("fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_work
                 "fa_decode_forward", "fa_decode_workspace_bytes", "fa_decode_split", "fa_decode_merge",
                 "fa_forward_window", "fa_backward_window", "fa_backward_dkdv_window", "fa_backward_dq_window",
                 "fa_decode_paged_forward", "fa_decode_paged_split", "fa_decode_paged_merge",
+                "fa_forward_blocksparse", "fa_backward_blocksparse", "fa_backward_dkdv_blocksparse",
+                "fa_backward_dq_blocksparse",
                 "fa_check_args", "fa_status_string")
 
 _lib = None
@@ -76,6 +78,14 @@ def load_library() -> ctypes.CDLL:
     for fn in (lib.fa_decode_paged_forward, lib.fa_decode_paged_split, lib.fa_decode_paged_merge):
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, i, i, i, f, vp]
         fn.restype = i
+    lib.fa_forward_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_forward_blocksparse.restype = i
+    lib.fa_backward_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
+    lib.fa_backward_blocksparse.restype = i
+    lib.fa_backward_dkdv_blocksparse.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_backward_dkdv_blocksparse.restype = i
+    lib.fa_backward_dq_blocksparse.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_backward_dq_blocksparse.restype = i
     lib.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i]
     lib.fa_check_args.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -112,9 +122,13 @@ def _require(t: torch.Tensor, name: str, dtype, shape):
                          f"got {t.dtype} {tuple(t.shape)} on {t.device} contiguous={t.is_contiguous()}")
 
 
-def forward(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None, window=None):
-    """bf16 forward via fa_forward (or fa_forward_window when ``window`` is given).
+def forward(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None, window=None, block_mask=None):
+    """bf16 forward via fa_forward (or fa_forward_window when ``window`` is given, or
+    fa_forward_blocksparse with a uint8 CUDA ``block_mask`` [nb, nb] over 64 x 64 blocks).
     Returns (o, lse); o bf16 [B,Hq,N,d], lse fp32 [B,Hq,N]."""
+    if block_mask is not None:
+        return _forward("fa_forward_blocksparse", torch.bfloat16, q, k, v, causal, scale, o, lse, stream,
+                        layout=_layout(block_mask, q.shape[2], q.device))
     if window is not None:
         return _forward("fa_forward_window", torch.bfloat16, q, k, v, causal, scale, o, lse, stream, window)
     return _forward("fa_forward", torch.bfloat16, q, k, v, causal, scale, o, lse, stream)
@@ -125,7 +139,15 @@ def forward_f32(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=No
     return _forward("fa_forward_f32", torch.float32, q, k, v, causal, scale, o, lse, stream)
 
 
-def _forward(fn, dtype, q, k, v, causal, scale, o, lse, stream, window=None):
+def _layout(block_mask, N, device):
+    nb = (N + 63) // 64
+    _require(block_mask, "block_mask", torch.uint8, (nb, nb))
+    if block_mask.device != device:
+        raise ValueError("block_mask must be on the same device as q")
+    return block_mask
+
+
+def _forward(fn, dtype, q, k, v, causal, scale, o, lse, stream, window=None, layout=None):
     lib = load_library()
     B, Hq, Hkv, N, d = _shape(q, k)
     _require(q, "q", dtype, (B, Hq, N, d))
@@ -138,7 +160,8 @@ def _forward(fn, dtype, q, k, v, causal, scale, o, lse, stream, window=None):
     _require(o, "o", dtype, (B, Hq, N, d))
     _require(lse, "lse", torch.float32, (B, Hq, N))
     extra = () if window is None else (int(window),)
-    code = getattr(lib, fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+    lay = () if layout is None else (layout.data_ptr(),)
+    code = getattr(lib, fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), *lay,
                             B, Hq, Hkv, N, d, int(causal), *extra, float(scale), _stream(stream))
     _check(fn, code)
     return o, lse
@@ -213,9 +236,9 @@ def workspace_bytes(B: int, Hq: int, N: int) -> int:
 
 
 def backward(q, k, v, o, do, lse, causal: bool, scale: float, dq=None, dk=None, dv=None,
-             workspace=None, stream=None, window=None):
-    """bf16 backward via fa_backward (or fa_backward_window when ``window`` is given).
-    Returns (dq, dk, dv)."""
+             workspace=None, stream=None, window=None, block_mask=None):
+    """bf16 backward via fa_backward (or fa_backward_window when ``window`` is given, or
+    fa_backward_blocksparse with ``block_mask``).  Returns (dq, dk, dv)."""
     lib = load_library()
     B, Hq, Hkv, N, d = _shape(q, k)
     for t, name, shp in ((q, "q", (B, Hq, N, d)), (k, "k", (B, Hkv, N, d)), (v, "v", (B, Hkv, N, d)),
@@ -233,8 +256,12 @@ def backward(q, k, v, o, do, lse, causal: bool, scale: float, dq=None, dk=None, 
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     fn = "fa_backward" if window is None else "fa_backward_window"
     extra = () if window is None else (int(window),)
+    lay = ()
+    if block_mask is not None:
+        fn = "fa_backward_blocksparse"
+        lay = (_layout(block_mask, N, q.device).data_ptr(),)
     code = getattr(lib, fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), *lay,
                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                             B, Hq, Hkv, N, d, int(causal), *extra, float(scale), _stream(stream))
     _check(fn, code)
@@ -242,7 +269,7 @@ def backward(q, k, v, o, do, lse, causal: bool, scale: float, dq=None, dk=None, 
 
 
 def backward_steps(q, k, v, o, do, lse, causal: bool, scale: float, dq, dk, dv, workspace,
-                   stream=None, steps=("pre", "dkdv", "dq"), window=None):
+                   stream=None, steps=("pre", "dkdv", "dq"), window=None, block_mask=None):
     """Enqueue the named backward steps (fa_backward_preprocess / _dkdv / _dq, or the
     _window forms of the last two when ``window`` is given) in order.
 
@@ -257,6 +284,16 @@ def backward_steps(q, k, v, o, do, lse, causal: bool, scale: float, dq, dk, dv, 
         if step == "pre":
             code = lib.fa_backward_preprocess(o.data_ptr(), do.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
                                               wsb, B, Hq, N, d, st)
+        elif step == "dkdv" and block_mask is not None:
+            code = lib.fa_backward_dkdv_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                                                    workspace.data_ptr(), wsb, dk.data_ptr(), dv.data_ptr(),
+                                                    _layout(block_mask, N, q.device).data_ptr(),
+                                                    B, Hq, Hkv, N, d, int(causal), float(scale), st)
+        elif step == "dq" and block_mask is not None:
+            code = lib.fa_backward_dq_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                                                  workspace.data_ptr(), wsb, dq.data_ptr(),
+                                                  _layout(block_mask, N, q.device).data_ptr(),
+                                                  B, Hq, Hkv, N, d, int(causal), float(scale), st)
         elif step == "dkdv":
             fn = "fa_backward_dkdv" if window is None else "fa_backward_dkdv_window"
             extra = () if window is None else (int(window),)

@@ -148,6 +148,7 @@ fa::FwdParams fwd_params(const void* q, const void* k, const void* v, void* o, f
     p.N = N;
     p.causal = causal;
     p.window = -1;
+    p.block_mask = nullptr;
     p.scale = scale;
     p.scale_log2 = kernel_scale_log2(scale);
     return p;
@@ -174,6 +175,7 @@ fa::BwdParams bwd_params(const void* q, const void* k, const void* v, const void
     p.N = N;
     p.causal = causal;
     p.window = -1;
+    p.block_mask = nullptr;
     p.scale = scale;
     p.scale_log2 = kernel_scale_log2(scale);
     return p;
@@ -415,6 +417,79 @@ fa_status fa_backward_dq_window(const void* q, const void* k, const void* v, con
         bwd_params(q, k, v, nullptr, dO, nullptr, dq, nullptr, nullptr, workspace, B, Hq, Hkv, N, causal, scale);
     p.window = kernel_window(window, N);
     return launched(fa::launch_bwd_dq(p, d, stream));
+}
+
+// Block-sparse calls: the layout must be present and cover at most 2048 x 2048
+// blocks; it is an input of every step, so no output may overlap it.
+static fa_status check_layout(const void* block_mask, const void* const* outs, const uintptr_t* out_bytes, int nout,
+                       int N) {
+    if (!block_mask) return FA_ERR_NULL;
+    const long long nb = (N + fa::kSparseBlockHost - 1) / fa::kSparseBlockHost;
+    if (nb > fa::kSparseMaxBlocksHost) return FA_ERR_SHAPE;
+    const uintptr_t lo = (uintptr_t)block_mask, hi = lo + (uintptr_t)(nb * nb);
+    for (int i = 0; i < nout; ++i) {
+        const uintptr_t lo2 = (uintptr_t)outs[i], hi2 = lo2 + out_bytes[i];
+        if (outs[i] && lo < hi2 && lo2 < hi) return FA_ERR_ALIAS;
+    }
+    return FA_OK;
+}
+
+fa_status fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const unsigned char* block_mask, int B, int Hq, int Hkv, int N, int d, int causal,
+                                 float scale, hipStream_t stream) {
+    fa_status s = check_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, 2);
+    if (s != FA_OK) return s;
+    const void* outs[2] = {o, lse};
+    const uintptr_t ob[2] = {(uintptr_t)B * Hq * N * d * 2, (uintptr_t)B * Hq * N * 4};
+    if ((s = check_layout(block_mask, outs, ob, 2, N)) != FA_OK) return s;
+    fa::FwdParams p = fwd_params(q, k, v, o, lse, B, Hq, Hkv, N, causal, scale);
+    p.block_mask = block_mask;
+    return launched(fa::launch_fwd_bf16(p, d, stream));
+}
+
+static fa_status bwd_blocksparse(int steps, const void* q, const void* k, const void* v, const void* o,
+                                 const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                                 const unsigned char* block_mask, void* workspace, size_t workspace_bytes, int B,
+                                 int Hq, int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
+    const BwdStep step = steps == 7 ? kAll : (steps == 2 ? kDkdv : kDq);
+    fa_status s = check_bwd(step, q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N, d,
+                            causal, scale);
+    if (s != FA_OK) return s;
+    const uintptr_t qb = (uintptr_t)B * Hq * N * d * 2, kb = (uintptr_t)B * Hkv * N * d * 2;
+    const void* outs[4] = {(steps & 4) ? dq : nullptr, (steps & 2) ? dk : nullptr, (steps & 2) ? dv : nullptr,
+                           (steps & 1) ? workspace : nullptr};
+    const uintptr_t ob[4] = {qb, kb, kb, workspace_bytes};
+    if ((s = check_layout(block_mask, outs, ob, 4, N)) != FA_OK) return s;
+    fa::BwdParams p = bwd_params(q, k, v, o, dO, lse, dq, dk, dv, workspace, B, Hq, Hkv, N, causal, scale);
+    p.block_mask = block_mask;
+    if ((steps & 1) && (s = launched(fa::launch_bwd_pre(p, d, stream))) != FA_OK) return s;
+    if ((steps & 2) && (s = launched(fa::launch_bwd_dkdv(p, d, stream))) != FA_OK) return s;
+    if (steps & 4) return launched(fa::launch_bwd_dq(p, d, stream));
+    return FA_OK;
+}
+
+fa_status fa_backward_blocksparse(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                                  const float* lse, void* dq, void* dk, void* dv, const unsigned char* block_mask,
+                                  void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
+                                  int causal, float scale, hipStream_t stream) {
+    return bwd_blocksparse(7, q, k, v, o, dO, lse, dq, dk, dv, block_mask, workspace, workspace_bytes, B, Hq, Hkv,
+                           N, d, causal, scale, stream);
+}
+
+fa_status fa_backward_dkdv_blocksparse(const void* q, const void* k, const void* v, const void* dO,
+                                       const void* workspace, size_t workspace_bytes, void* dk, void* dv,
+                                       const unsigned char* block_mask, int B, int Hq, int Hkv, int N, int d,
+                                       int causal, float scale, hipStream_t stream) {
+    return bwd_blocksparse(2, q, k, v, nullptr, dO, nullptr, nullptr, dk, dv, block_mask, (void*)workspace,
+                           workspace_bytes, B, Hq, Hkv, N, d, causal, scale, stream);
+}
+
+fa_status fa_backward_dq_blocksparse(const void* q, const void* k, const void* v, const void* dO,
+                                     const void* workspace, size_t workspace_bytes, void* dq,
+                                     const unsigned char* block_mask, int B, int Hq, int Hkv, int N, int d,
+                                     int causal, float scale, hipStream_t stream) {
+    return bwd_blocksparse(4, q, k, v, nullptr, dO, nullptr, dq, nullptr, nullptr, block_mask, (void*)workspace,
+                           workspace_bytes, B, Hq, Hkv, N, d, causal, scale, stream);
 }
 
 fa_status fa_backward_preprocess(const void* o, const void* dO, const float* lse, void* workspace,

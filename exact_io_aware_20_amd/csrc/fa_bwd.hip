@@ -35,7 +35,8 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x 
 
 // ---------------------------------------------------------------------------------
 // Per query row: D_i = sum_t dO_it * O_it (fp32) and LSE_i * log2(e).  D/8 lanes
-// per row, 16 bytes per lane.
+// per row, 16 bytes per lane.  A row that saw no key (LSE = -inf, possible under a
+// block-sparse layout) gets +inf instead, so that its recomputed P = 2^(S - inf) is 0.
 // ---------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void fa_bwd_pre_kernel(const uint16_t* o, const uint16_t* dO,
@@ -58,7 +59,10 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_pre_kernel(const uint16_t* o,
 #pragma unroll
     for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
     if (row < rows && sub == 0) dsum[row] = acc;
-    if (row < rows && sub == 1) lse2[row] = lse[row] * kLog2e;
+    if (row < rows && sub == 1) {
+        const float l = lse[row];
+        lse2[row] = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
+    }
 }
 
 // ---------------------------------------------------------------------------------
@@ -144,8 +148,9 @@ __device__ __forceinline__ void acc_half(const uint16_t* tt, const u32x4 (&bf)[2
 //   P/dV: P(it) to LDS, dV MFMAs;       dS/dK: dS and dK MFMAs of item it-1.
 // In each half one wave of a SIMD pair runs exponentials or dS while the other
 // runs matrix work.
-template <int D, bool PV>
-__device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, int wave, int lane) {
+template <int D, bool PV, bool SPARSE>
+__device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, const uint32_t* list, int list_n,
+                                          int wave, int lane) {
     using C = DkdvCfg<D>;
     const int l32 = lane & 31;
     const int hh = lane >> 5;
@@ -174,14 +179,20 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, in
     // query tiles holding a row that sees one of the workgroup's keys
     const int wl = band_left(p), wr = band_right(p);
     const int qt_start = max(0, k0 - wr) / C::BQ;
-    const int per_head = min(N - 1, k0 + C::BK - 1 + wl) / C::BQ + 1 - qt_start;
+    // block-sparse: the compacted list of query tiles that see one of the workgroup's
+    // two key tiles (bit 20 + j: key tile j sees it)
+    const int per_head = SPARSE ? list_n : min(N - 1, k0 + C::BK - 1 + wl) / C::BQ + 1 - qt_start;
+    const uint32_t wbit = 20u + (uint32_t)((wave & 3) >> 1);
     const int nitems = G * per_head;
     const float sl2 = p.scale_log2;
     float* pbuf = (float*)(smem + C::NSTAGE * C::STAGE) + (wave & 3) * 32 * 64;   // this pair's P slots
 
     TileDma<D, 1, C::WAVES> dma;
     dma.init(wave, lane);
-    auto item_q0 = [&](int it) { return (qt_start + it % per_head) * C::BQ; };
+    auto item_q0 = [&](int it) {
+        if constexpr (SPARSE) return (int)(list[it % per_head] & kSparseTileMask) * C::BQ;
+        return (qt_start + it % per_head) * C::BQ;
+    };
     auto issue_item = [&](int it) {
         const int hq = hkv * G + it / per_head;
         const int q0 = item_q0(it);
@@ -206,7 +217,8 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, in
         const uint16_t* st = smem + ((mine + C::NSTAGE) % C::NSTAGE) * C::STAGE;
         const float* lse2 = (const float*)(st + 2 * C::NAT);
         const float* dvec = lse2 + C::BQ;
-        const bool act = have && active(q0);
+        bool act = have && active(q0);
+        if constexpr (SPARSE) act = act && ((list[(mine < 0 ? 0 : mine) % per_head] >> wbit) & 1u);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();                                               // A
         if (it + 1 < nitems) issue_item(it + 1);
@@ -289,18 +301,45 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, in
     }
 }
 
-template <int D>
+template <int D, bool SPARSE>
 __global__ __launch_bounds__(DkdvCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
     using C = DkdvCfg<D>;
     __shared__ __attribute__((aligned(16))) uint16_t smem[C::NSTAGE * C::STAGE + C::PBUF];
+    __shared__ uint32_t list[SPARSE ? kSparseMaxBlocks : 1];
+    __shared__ int list_n;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     __builtin_assume(wave < C::WAVES);
+    int n = 0;
+    if constexpr (SPARSE) {
+        // query tiles u that see key tile kt0 + j of this workgroup (layout bit set,
+        // and not before the key tile under the causal rule)
+        const int N = p.N;
+        const int nb = (N + kSparseBlock - 1) / kSparseBlock;
+        const int ntile_k = (N + C::BK - 1) / C::BK;
+        int head_kv, kt;
+        map_block(blockIdx.x, gridDim.x, ntile_k, p.B * p.Hkv, false, head_kv, kt, 4);
+        const int kt0 = kt * (C::BK / kSparseBlock);
+        if (wave == 0) {
+            const int c = compact_tiles(list, nb, tid & 63, [&](int u) -> uint32_t {
+                uint32_t bits = 0;
+#pragma unroll
+                for (int j = 0; j < C::BK / kSparseBlock; ++j) {
+                    const int kb = kt0 + j;
+                    if (kb < nb && (!p.causal || u >= kb) && p.block_mask[(size_t)u * nb + kb]) bits |= 1u << j;
+                }
+                return bits;
+            });
+            if ((tid & 63) == 0) list_n = c;
+        }
+        __syncthreads();
+        n = list_n;
+    }
     if (wave < 4)
-        dkdv_role<D, true>(p, smem, wave, tid & 63);
+        dkdv_role<D, true, SPARSE>(p, smem, list, n, wave, tid & 63);
     else
-        dkdv_role<D, false>(p, smem, wave, tid & 63);
+        dkdv_role<D, false, SPARSE>(p, smem, list, n, wave, tid & 63);
 }
 
 // ---------------------------------------------------------------------------------
@@ -322,13 +361,15 @@ struct DqCfg {
 // dQ kernel: per key/value tile, S^T = K Q^T and dP^T = V dO^T (lane: query),
 // dS^T = P^T (dP^T - D) rounded to bf16, dQ^T += K^T dS^T with K^T read transposed
 // from the natural K tile.  K/V tiles are double-buffered with one barrier each.
-template <int D>
+template <int D, bool SPARSE>
 __global__ __launch_bounds__(DqCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(BwdParams p) {
     using C = DqCfg<D>;
     using KS = SwzTile<D, 1>;
     using VS = SwzTile<D, 0>;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::STAGE];
+    __shared__ uint32_t list[SPARSE ? kSparseMaxBlocks : 1];
+    __shared__ int list_n;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -385,15 +426,42 @@ void fa_bwd_dq_kernel(BwdParams p) {
         vdma.issue(Vh + (size_t)k0 * D, N - k0, st + C::KT, wave);
     };
 
-    load_tile(t_begin, smem + (t_begin & 1) * C::STAGE);
-    for (int t = t_begin; t < ntiles; ++t) {
-        const int k0 = t * C::BC;
-        const uint16_t* st = smem + (t & 1) * C::STAGE;
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();                       // tile t landed; stage (t+1)&1 free
-        if (t + 1 < ntiles) load_tile(t + 1, smem + ((t + 1) & 1) * C::STAGE);
+    // Entries e in [e_begin, e_end): the key tiles t_begin .. ntiles-1, or under a
+    // block-sparse layout the compacted list of key tiles that one of the workgroup's
+    // four 64-row blocks sees (bit 20 + j: block j sees it).
+    int e_begin = t_begin, e_end = ntiles;
+    if constexpr (SPARSE) {
+        const int nb = (N + kSparseBlock - 1) / kSparseBlock;
+        const int qb0 = q0 / kSparseBlock;
+        if (wave == 0) {
+            const int c = compact_tiles(list, nb, lane, [&](int u) -> uint32_t {
+                uint32_t bits = 0;
+#pragma unroll
+                for (int j = 0; j < C::BR / kSparseBlock; ++j) {
+                    const int qb = qb0 + j;
+                    if (qb < nb && (!p.causal || u <= qb) && p.block_mask[(size_t)qb * nb + u]) bits |= 1u << j;
+                }
+                return bits;
+            });
+            if (lane == 0) list_n = c;
+        }
+        __syncthreads();
+        e_begin = 0;
+        e_end = list_n;
+    }
+    const uint32_t wbit = 20u + (uint32_t)(wave / (kSparseBlock / 32));
+    auto tile_of = [&](int e) { return SPARSE ? (int)(list[e] & kSparseTileMask) : e; };
 
-        if (t < wave_tiles) {
+    if (e_begin < e_end) load_tile(tile_of(e_begin), smem + (e_begin & 1) * C::STAGE);
+    for (int e = e_begin; e < e_end; ++e) {
+        const int t = tile_of(e);
+        const int k0 = t * C::BC;
+        const uint16_t* st = smem + (e & 1) * C::STAGE;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();                       // tile e landed; stage (e+1)&1 free
+        if (e + 1 < e_end) load_tile(tile_of(e + 1), smem + ((e + 1) & 1) * C::STAGE);
+
+        if (t < wave_tiles && (!SPARSE || ((list[e] >> wbit) & 1u))) {
             f32x16 s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
 #pragma unroll
             for (int c = 0; c < C::DC; ++c)
@@ -472,7 +540,10 @@ static hipError_t launch_pre(const BwdParams& p, hipStream_t stream) {
 template <int D>
 static hipError_t launch_dkdv(const BwdParams& p, hipStream_t stream) {
     const unsigned blocks = (unsigned)((long long)p.B * p.Hkv * ((p.N + DkdvCfg<D>::BK - 1) / DkdvCfg<D>::BK));
-    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<D>, dim3(blocks), dim3(DkdvCfg<D>::THREADS), 0, stream, p);
+    if (p.block_mask)
+        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, true>), dim3(blocks), dim3(DkdvCfg<D>::THREADS), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, false>), dim3(blocks), dim3(DkdvCfg<D>::THREADS), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -480,7 +551,10 @@ template <int D>
 static hipError_t launch_dq(const BwdParams& p, hipStream_t stream) {
     constexpr int br = DqCfg<D>::BR;
     const unsigned blocks = (unsigned)((long long)p.B * p.Hq * ((p.N + br - 1) / br));
-    hipLaunchKernelGGL(fa_bwd_dq_kernel<D>, dim3(blocks), dim3(DqCfg<D>::THREADS), 0, stream, p);
+    if (p.block_mask)
+        hipLaunchKernelGGL((fa_bwd_dq_kernel<D, true>), dim3(blocks), dim3(DqCfg<D>::THREADS), 0, stream, p);
+    else
+        hipLaunchKernelGGL((fa_bwd_dq_kernel<D, false>), dim3(blocks), dim3(DqCfg<D>::THREADS), 0, stream, p);
     return hipGetLastError();
 }
 

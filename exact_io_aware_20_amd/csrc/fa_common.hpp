@@ -202,4 +202,31 @@ __device__ __forceinline__ u32x4 tr_frag(const uint16_t* tile, int db, int kk, i
     return cat(lo, hi);
 }
 
+// ---------------------------------------------------------------------------------
+// Block-sparse layouts: a 0/1 byte matrix over 64 x 64 blocks of (query, key)
+// positions, nb x nb with nb = ceil(N / 64), shared by every (batch, head).  A
+// workgroup first compacts the tiles it has to visit into an LDS list.
+// ---------------------------------------------------------------------------------
+constexpr int kSparseBlock = 64;
+constexpr int kSparseMaxBlocks = 2048;   // N <= 131072
+constexpr uint32_t kSparseTileMask = (1u << 20) - 1;
+
+// One wave, lanes over the candidates u in [0, n): bits(u) returns a small bit set
+// (which of the workgroup's blocks see candidate u; 0 = none).  Entries
+// u | bits << 20 are appended to `list` in increasing u; returns their number (the
+// same in every lane).
+template <typename F>
+__device__ __forceinline__ int compact_tiles(uint32_t* list, int n, int lane, F bits) {
+    int cnt = 0;
+    for (int base = 0; base < n; base += kWave) {
+        const int u = base + lane;
+        const uint32_t b = u < n ? bits(u) : 0u;
+        const uint64_t m = __ballot(b != 0u);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (b != 0u) list[cnt + below] = (uint32_t)u | (b << 20);
+        cnt += __popcll(m);
+    }
+    return cnt;
+}
+
 }  // namespace fa

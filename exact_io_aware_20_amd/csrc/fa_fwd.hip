@@ -225,6 +225,122 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------------
+// Block-sparse forward (page "ZeRO 与 FlashAttention 各优化什么?", section
+// "注意力瓶颈与优化路线": block-sparse patterns compute only part of the positions).
+// The workgroup's 256 rows are four 64-row blocks of the layout; wave 0 compacts the
+// key tiles that any of them sees (layout bit set, and not after the block under the
+// causal rule) into an LDS list, tagged with which blocks see each, and the workgroup
+// walks that list with the per-tile steps above: K/V double-buffered, one barrier per
+// tile, and a wave computes only the tiles its own block sees.  A row that sees no key
+// gets O = 0 and LSE = -inf.
+// ---------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(FwdCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_sparse_kernel(FwdParams p) {
+    using C = FwdCfg<D>;
+    constexpr int KB = SwzTile<D, 0>::ELEMS;
+    constexpr int VB = SwzTile<D, 1>::ELEMS;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * KB + 2 * VB];
+    __shared__ uint32_t list[kSparseMaxBlocks];
+    __shared__ int list_n;
+    uint16_t* kbuf = smem;
+    uint16_t* vbuf = smem + 2 * KB;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(wave < C::WAVES);
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+    const int N = p.N;
+    const int wr = p.causal ? 0 : N;
+
+    const int ntile_q = (N + C::BR - 1) / C::BR;
+    int head, qt;
+    map_block(blockIdx.x, gridDim.x, ntile_q, p.B * p.Hq, p.causal != 0, head, qt, 4);
+    const int hq = head % p.Hq;
+    const int b = head / p.Hq;
+    const int hkv = hq / (p.Hq / p.Hkv);
+    const uint16_t* Qh = (const uint16_t*)p.q + (size_t)head * N * D;
+    const uint16_t* Kh = (const uint16_t*)p.k + ((size_t)b * p.Hkv + hkv) * N * D;
+    const uint16_t* Vh = (const uint16_t*)p.v + ((size_t)b * p.Hkv + hkv) * N * D;
+
+    const int q0 = qt * C::BR;
+    const int qw0 = q0 + wave * 32;
+    const int q = qw0 + l32;
+    const int nb = (N + kSparseBlock - 1) / kSparseBlock;
+    const int qb0 = q0 / kSparseBlock;
+    if (wave == 0) {
+        const int n = compact_tiles(list, nb, lane, [&](int u) -> uint32_t {
+            uint32_t bits = 0;
+#pragma unroll
+            for (int j = 0; j < C::BR / kSparseBlock; ++j) {
+                const int qb = qb0 + j;
+                if (qb < nb && (!p.causal || u <= qb) && p.block_mask[(size_t)qb * nb + u]) bits |= 1u << j;
+            }
+            return bits;
+        });
+        if (lane == 0) list_n = n;
+    }
+    __syncthreads();
+    const int cnt = list_n;
+    const int wbit = 20 + wave / (kSparseBlock / 32);   // this wave's block within the workgroup
+
+    u32x4 qf[C::DC];
+#pragma unroll
+    for (int c = 0; c < C::DC; ++c)
+        qf[c] = q < N ? ld_global16(Qh + (size_t)q * D + 16 * c + 8 * hh) : zero_u4();
+    f32x16 o[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) o[db] = zero16();
+    float m_ref = kNegInf, l_part = 0.f;
+    const float sl2 = p.scale_log2;
+
+    TileDma<D, 0, C::WAVES> kdma;
+    TileDma<D, 1, C::WAVES> vdma;
+    kdma.init(wave, lane);
+    vdma.init(wave, lane);
+    auto load_tile = [&](int e) {
+        const int t = (int)(list[e] & kSparseTileMask);
+        kdma.issue(Kh + (size_t)t * C::BC * D, N - t * C::BC, kbuf + (e & 1) * KB, wave);
+        vdma.issue(Vh + (size_t)t * C::BC * D, N - t * C::BC, vbuf + (e & 1) * VB, wave);
+    };
+    if (cnt > 0) load_tile(0);
+    for (int e = 0; e < cnt; ++e) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();                       // tile e landed; the other buffers are free
+        if (e + 1 < cnt) load_tile(e + 1);
+        const uint32_t ent = list[e];
+        const int k0 = (int)(ent & kSparseTileMask) * C::BC;
+        if (((ent >> wbit) & 1u) && qw0 < N) {
+            f32x16 sc[2];
+            fwd_scores<D>(kbuf + (e & 1) * KB, qf, sc, l32, hh);
+            if (k0 + C::BC - 1 > qw0 + wr || k0 + C::BC > N) fwd_mask<false>(sc, k0, 0, min(q + wr, N - 1), hh);
+            fwd_rescale<D>(sc, o, m_ref, l_part, sl2);
+            u32x4 pf[2][2];
+            fwd_probs(sc, m_ref, sl2, pf, l_part);
+            fwd_pv<D>(vbuf + (e & 1) * VB, pf, o, lane);
+        }
+    }
+
+    const float lt = l_part + __shfl_xor(l_part, 32);
+    if (q < N) {
+        const bool any = lt > 0.f;
+        uint16_t* Oh = (uint16_t*)p.o + (size_t)head * N * D + (size_t)q * D;
+        const float inv = any ? 1.0f / lt : 0.f;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const u32x2 v2 = {pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                                  pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+                *(u32x2*)(Oh + 32 * db + 8 * g + 4 * hh) = v2;
+            }
+        if (hh == 0) p.lse[(size_t)head * N + q] = any ? (m_ref + __log2f(lt)) * kLn2 : kNegInf;
+    }
+}
+
+// ---------------------------------------------------------------------------------
 // fp32 forward: every value in fp32, vector ALU only.  Two lanes share a query
 // row (each holds half of d); 32 rows per wave, K/V tiles of 32 keys in LDS.
 // ---------------------------------------------------------------------------------
@@ -313,7 +429,9 @@ template <int D>
 static hipError_t launch_bf16(const FwdParams& p, hipStream_t stream) {
     constexpr int br = FwdCfg<D>::BR;
     const long long nblk = (long long)p.B * p.Hq * ((p.N + br - 1) / br);
-    if (p.window >= 0)
+    if (p.block_mask)
+        hipLaunchKernelGGL((fa_fwd_sparse_kernel<D>), dim3((unsigned)nblk), dim3(FwdCfg<D>::THREADS), 0, stream, p);
+    else if (p.window >= 0)
         hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, true>), dim3((unsigned)nblk), dim3(FwdCfg<D>::THREADS), 0, stream,
                            p);
     else

@@ -5,6 +5,11 @@
 
 namespace fa {
 
+// Block-sparse layouts: side of a block and the largest layout (host-side copies of
+// the device constants).
+constexpr int kSparseBlockHost = 64;
+constexpr int kSparseMaxBlocksHost = 2048;
+
 struct FwdParams {
     const void* q;
     const void* k;
@@ -13,6 +18,7 @@ struct FwdParams {
     float* lse;
     int B, Hq, Hkv, N, causal;
     int window;         // sliding window: key j visible to query i only if |i - j| <= window; < 0: none
+    const uint8_t* block_mask;   // block-sparse layout [nb][nb] over 64 x 64 blocks, or null
     float scale;        // softmax scale
     float scale_log2;   // scale * log2(e)
 };
@@ -31,6 +37,7 @@ struct BwdParams {
     float* lse2;        // workspace: LSE_i * log2(e), one fp32 per query row
     int B, Hq, Hkv, N, causal;
     int window;         // as in FwdParams
+    const uint8_t* block_mask;   // as in FwdParams
     float scale;
     float scale_log2;
 };

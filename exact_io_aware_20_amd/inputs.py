@@ -18,6 +18,7 @@ decode_gqa_kv65536_d128       8    24    2  65536  128  yes     bf16   decode, N
 decode_spec4_kv65536_d128     8    24    2  65536  128  yes     bf16   decode, Nq=4
 window_n16384_w2047_d128      2    16   16  16384  128  yes     bf16   fwd, bwd (window 2047)
 decode_paged_kv65536_d128    16    24    2  65536  128  yes     bf16   paged decode, Nq=1
+blocksparse_n16384_d128       2    16   16  16384  128  yes     bf16   fwd, bwd (local + global)
 ==========================  ====  ===  ===  =====  ===  ======  =====  ===========
 
 The long-context workload multiplies q and k by 8 before the cast (a power of two,
@@ -28,7 +29,9 @@ head; q is [B, Hq, Nq, d] and k, v are [B, Hkv, N, d].  The window workload lets
 query see only keys within 2047 positions (with the causal rule: its 2048 most recent
 tokens, itself included).  The paged decode workload holds 16 sequences of seeded
 lengths between 2048 and 65536 tokens (the first exactly 65536) in 256-token pages
-scattered over a pool by a seeded permutation; unused table entries are -1.
+scattered over a pool by a seeded permutation; unused table entries are -1.  The
+block-sparse workload's layout over 64 x 64 blocks is local + global: a query block
+sees its own block and the 7 before it, and the first 2 key blocks.
 """
 from __future__ import annotations
 
@@ -55,6 +58,7 @@ class Workload:
     nq: int = 0            # decode: query rows per head (0: the queries are the whole sequence)
     window: int = -1       # sliding window |i - j| <= window (-1: none)
     page_size: int = 0     # paged decode: tokens per page (0: contiguous cache); N is the longest sequence
+    layout: tuple = ()     # block-sparse: (local blocks, global blocks) of local_global_layout
 
     @property
     def decode(self) -> bool:
@@ -82,6 +86,7 @@ WORKLOADS = {
         Workload("window_n16384_w2047_d128", 8000, 2, 16, 16, 16384, 128, (True,), "bf16", True, window=2047),
         Workload("decode_paged_kv65536_d128", 9000, 16, 24, 2, 65536, 128, (True,), "bf16", False, nq=1,
                  page_size=256),
+        Workload("blocksparse_n16384_d128", 10000, 2, 16, 16, 16384, 128, (True,), "bf16", True, layout=(8, 2)),
     )
 }
 
@@ -149,3 +154,23 @@ def paged_cache(B, Hq, Hkv, Nq, max_len, d, page_size, seed_base: int, min_len: 
 
 def paged_workload_inputs(w: Workload) -> dict:
     return paged_cache(w.B, w.Hq, w.Hkv, w.nq, w.N, w.d, w.page_size, w.seed_base, min_len=2048)
+
+
+def local_global_layout(N: int, local: int, nglobal: int) -> torch.Tensor:
+    """uint8 [nb, nb] over 64 x 64 blocks (nb = ceil(N/64)): query block i sees key
+    blocks j with |i - j| < local (a local band) and the first ``nglobal`` key blocks."""
+    nb = (N + 63) // 64
+    i = torch.arange(nb)[:, None]
+    j = torch.arange(nb)[None, :]
+    return (((i - j).abs() < local) | (j < nglobal)).to(torch.uint8)
+
+
+def random_layout(N: int, density: float, seed: int) -> torch.Tensor:
+    """uint8 [nb, nb] with each block set independently with probability ``density``."""
+    nb = (N + 63) // 64
+    g = torch.Generator().manual_seed(int(seed))
+    return (torch.rand(nb, nb, generator=g) < density).to(torch.uint8)
+
+
+def workload_layout(w: Workload) -> torch.Tensor:
+    return local_global_layout(w.N, *w.layout)

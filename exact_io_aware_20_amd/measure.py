@@ -106,3 +106,28 @@ def paged_split_bytes(seq_lens, B, Hq, Hkv, Nq, d, elt: int) -> int:
     """The paged split kernel's algorithmic traffic: Q and the cached K/V read once."""
     tokens = int(sum(int(n) for n in seq_lens))
     return elt * (B * Hq * Nq * d + 2 * Hkv * tokens * d)
+
+
+def layout_pairs(N, layout, causal: bool, block: int = 64) -> int:
+    """Visible (query, key) pairs under a block-sparse layout [nb][nb] (and the causal
+    rule): each set block pair contributes its rows x keys, or rows(rows+1)/2 on the
+    diagonal under the causal rule and nothing above it."""
+    import numpy as np
+    lay = np.asarray(layout).astype(bool)
+    nb = lay.shape[0]
+    size = np.minimum(block, N - block * np.arange(nb))
+    total = 0
+    for i in range(nb):
+        for j in np.nonzero(lay[i])[0]:
+            if causal and j > i:
+                continue
+            if causal and j == i:
+                total += int(size[i]) * (int(size[i]) + 1) // 2
+            else:
+                total += int(size[i]) * int(size[j])
+    return total
+
+
+def layout_fwd_flops(B, Hq, N, d, causal: bool, layout) -> float:
+    """Forward of a block-sparse call: two contractions over the visible pairs."""
+    return 4.0 * B * Hq * d * layout_pairs(N, layout, causal)

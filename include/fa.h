@@ -157,6 +157,39 @@ fa_status fa_backward_dq_window(const void* q, const void* k, const void* v, con
                                 int window, float scale, hipStream_t stream);
 
 /*
+ * Block-sparse attention: as fa_forward / fa_backward (and its dK/dV and dQ steps),
+ * with key j visible to query i only if block_mask[(i/64)*nb + j/64] is nonzero, on
+ * top of the causal rule (page "ZeRO 与 FlashAttention 各优化什么?",
+ * "注意力瓶颈与优化路线": block-sparse and global + local patterns compute only part of
+ * the positions).  block_mask: device bytes [nb][nb], nb = ceil(N/64) <= 2048 (so
+ * N <= 131072, FA_ERR_SHAPE beyond), shared by every batch and head, read only.
+ * Blocks whose byte is 0 are neither loaded nor computed.  A query that sees no key
+ * gets O = 0 and LSE = -inf, and contributes nothing to the gradients.  Other
+ * arguments, layouts and errors are those of the dense calls; the backward takes lse
+ * from fa_forward_blocksparse with the same layout, and the dK/dV and dQ steps take
+ * the workspace of fa_backward_preprocess.
+ */
+fa_status fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 const unsigned char* block_mask,
+                                 int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                                 hipStream_t stream);
+fa_status fa_backward_blocksparse(const void* q, const void* k, const void* v, const void* o,
+                                  const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                                  const unsigned char* block_mask, void* workspace, size_t workspace_bytes,
+                                  int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                                  hipStream_t stream);
+fa_status fa_backward_dkdv_blocksparse(const void* q, const void* k, const void* v, const void* dO,
+                                       const void* workspace, size_t workspace_bytes, void* dk, void* dv,
+                                       const unsigned char* block_mask,
+                                       int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                                       hipStream_t stream);
+fa_status fa_backward_dq_blocksparse(const void* q, const void* k, const void* v, const void* dO,
+                                     const void* workspace, size_t workspace_bytes, void* dq,
+                                     const unsigned char* block_mask,
+                                     int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                                     hipStream_t stream);
+
+/*
  * Decode forward: Nq new queries per head against a cache of Nk keys and values.
  *
  * The queries are the last Nq tokens of a sequence whose Nk keys and values, their

@@ -203,3 +203,21 @@ def test_paged_decode_rejects_before_launch():
     assert call(wsb=need - 4) == 8
     assert call(o=KP) == 9               # o overlaps the K pool
     assert call(Nq=1001) == 2            # causal: more queries than the longest sequence
+
+
+def test_blocksparse_calls_reject_before_launch():
+    lib = api.load_library()
+    dO, ws, dq, dk, dv, BM = (0x20_0000_0000, 0x60_0000_0000, 0x30_0000_0000, 0x40_0000_0000, 0x50_0000_0000,
+                              0x80_0000_0000)
+    need = lib.fa_backward_workspace_bytes(1, 2, 16)
+    assert lib.fa_forward_blocksparse(Q, K, V, O, L, None, 1, 2, 1, 16, 64, 1, 0.1, None) == 1
+    assert lib.fa_forward_blocksparse(Q, K, V, O, L, BM, 1, 2, 1, 200000, 64, 1, 0.1, None) == 2   # > 2048 blocks
+    assert lib.fa_forward_blocksparse(Q, K, V, O, L, O, 1, 2, 1, 16, 64, 1, 0.1, None) == 9        # layout = o
+    assert lib.fa_forward_blocksparse(Q, K, V, O, L, BM, 1, 2, 1, 16, 80, 1, 0.1, None) == 4
+    assert lib.fa_backward_blocksparse(Q, K, V, O, dO, L, dq, dk, dv, None, ws, need, 1, 2, 1, 16, 64, 1, 0.1,
+                                       None) == 1
+    assert lib.fa_backward_blocksparse(Q, K, V, O, dO, L, dq, dk, dv, dq, ws, need, 1, 2, 1, 16, 64, 1, 0.1,
+                                       None) == 9
+    assert lib.fa_backward_dkdv_blocksparse(Q, K, V, dO, ws, need - 4, dk, dv, BM, 1, 2, 1, 16, 64, 1, 0.1,
+                                            None) == 8
+    assert lib.fa_backward_dq_blocksparse(Q, K, V, dO, ws, need, dq, BM, 1, 3, 2, 16, 64, 1, 0.1, None) == 3

@@ -1,0 +1,133 @@
+"""Parity of the block-sparse path (fa_forward_blocksparse / fa_backward_blocksparse,
+through the C ABI) with the CPU float64 oracle's block layout: key j visible to
+query i only if layout[i // 64][j // 64] (and j <= i when causal).
+
+Bars (as for the dense bf16 path): |O - O_ref| <= 1e-2 + half a bf16 ulp,
+|LSE - LSE_ref| <= 1e-2 (rows that see no key: O = 0 and LSE = -inf on both sides),
+relative L2 <= 1e-2 for dQ, dK and dV.  Small cases use seeded random layouts (with
+empty block rows), ragged lengths, grouped-query heads, both head sizes and both
+mask settings; the local + global workload is checked at full size on sampled rows
+and two KV groups.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_20_amd import api, inputs
+from tests.test_parity_gpu import WORKERS, assert_o_bf16, dev, f64, make, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write(f"\n[gpu-case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+
+
+def lse_error(lse, lse_ref):
+    fin = np.isfinite(lse_ref)
+    assert np.isneginf(lse[~fin]).all()
+    return float(np.abs(lse[fin] - lse_ref[fin]).max()) if fin.any() else 0.0
+
+
+CASES = [  # (B, Hq, Hkv, N, d, density)
+    (1, 1, 1, 64, 128, 1.0), (1, 2, 1, 130, 64, 0.5), (2, 4, 2, 300, 128, 0.4), (1, 3, 1, 513, 128, 0.3),
+    (1, 2, 2, 1000, 64, 0.25), (1, 4, 2, 777, 128, 0.6),
+]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_blocksparse_small(case, causal):
+    B, Hq, Hkv, N, d, density = case
+    host, g = make(B, Hq, Hkv, N, d, seed=16000 + N, with_do=True)
+    lay = inputs.random_layout(N, density, 16100 + N)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = api.forward(g["q"], g["k"], g["v"], causal, scale, block_mask=lay.to(dev()))
+    dq, dk, dv = api.backward(g["q"], g["k"], g["v"], o, g["do"], lse, causal, scale, block_mask=lay.to(dev()))
+    torch.cuda.synchronize()
+    bm = lay.numpy().astype(bool)
+    o_ref, lse_ref = oracle.attention_forward(host["q"], host["k"], host["v"], causal, scale, block_mask=bm)
+    err = assert_o_bf16(f64(o), o_ref, str(case))
+    lerr = lse_error(f64(lse), lse_ref)
+    ref = oracle.attention_backward(host["q"], host["k"], host["v"], host["do"], causal, scale, block_mask=bm)
+    errs = {n: (rel_l2(f64(a), r) if np.abs(r).max() > 0 else float(np.abs(f64(a)).max()))
+            for n, a, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref)}
+    print(f"[parity] blocksparse {case} causal={causal} O {err:.3e} LSE {lerr:.3e} "
+          + " ".join(f"{k} {v:.3e}" for k, v in errs.items()))
+    assert lerr <= 1e-2 and max(errs.values()) <= 1e-2
+
+
+def test_blocksparse_empty_rows_and_empty_layout():
+    # block rows with no set block (and, under the causal rule, only blocks after
+    # themselves) see no key: O = 0, LSE = -inf, and they add nothing to dK/dV
+    B, Hq, Hkv, N, d = 1, 2, 1, 256, 128
+    host, g = make(B, Hq, Hkv, N, d, seed=16500, with_do=True)
+    lay = torch.tensor([[0, 1, 0, 0], [1, 1, 0, 0], [0, 0, 0, 0], [1, 0, 1, 1]], dtype=torch.uint8)
+    o, lse = api.forward(g["q"], g["k"], g["v"], True, 0.09, block_mask=lay.to(dev()))
+    dq, dk, dv = api.backward(g["q"], g["k"], g["v"], o, g["do"], lse, True, 0.09, block_mask=lay.to(dev()))
+    torch.cuda.synchronize()
+    o_h, l_h = f64(o), f64(lse)
+    assert (o_h[:, :, :64] == 0).all() and np.isneginf(l_h[:, :, :64]).all()
+    assert (o_h[:, :, 128:192] == 0).all() and np.isneginf(l_h[:, :, 128:192]).all()
+    assert (f64(dq)[:, :, :64] == 0).all() and np.isfinite(f64(dk)).all() and np.isfinite(f64(dv)).all()
+    bm = lay.numpy().astype(bool)
+    ref = oracle.attention_backward(host["q"], host["k"], host["v"], host["do"], True, 0.09, block_mask=bm)
+    for a, r in zip((dq, dk, dv), ref):
+        assert rel_l2(f64(a), r) <= 1e-2
+    zero = torch.zeros_like(lay)
+    o0, l0 = api.forward(g["q"], g["k"], g["v"], False, 0.09, block_mask=zero.to(dev()))
+    torch.cuda.synchronize()
+    assert (f64(o0) == 0).all() and np.isneginf(f64(l0)).all()
+
+
+def test_blocksparse_steps_match_fused_call():
+    B, Hq, Hkv, N, d = 1, 4, 2, 700, 128
+    host, g = make(B, Hq, Hkv, N, d, seed=16600, with_do=True)
+    lay = inputs.random_layout(N, 0.4, 16601).to(dev())
+    o, lse = api.forward(g["q"], g["k"], g["v"], True, 0.09, block_mask=lay)
+    dq, dk, dv = api.backward(g["q"], g["k"], g["v"], o, g["do"], lse, True, 0.09, block_mask=lay)
+    dq2, dk2, dv2 = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+    ws = torch.empty(api.workspace_bytes(B, Hq, N), dtype=torch.uint8, device=dev())
+    api.backward_steps(g["q"], g["k"], g["v"], o, g["do"], lse, True, 0.09, dq2, dk2, dv2, ws, block_mask=lay)
+    torch.cuda.synchronize()
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_blocksparse_workload_full_size():
+    w = inputs.WORKLOADS["blocksparse_n16384_d128"]
+    host = inputs.workload_inputs(w)
+    g = {k: v.to(dev()) for k, v in host.items()}
+    lay = inputs.workload_layout(w)
+    o, lse = api.forward(g["q"], g["k"], g["v"], True, w.scale, block_mask=lay.to(dev()))
+    dq, dk, dv = api.backward(g["q"], g["k"], g["v"], o, g["do"], lse, True, w.scale, block_mask=lay.to(dev()))
+    torch.cuda.synchronize()
+    bm = lay.numpy().astype(bool)
+    rng = np.random.default_rng(10)
+    rows = np.unique(np.concatenate([np.arange(256), np.arange(w.N - 256, w.N), rng.choice(w.N, 1024, replace=False)]))
+    heads = [(0, 1), (1, 14)]
+    o_ref, lse_ref = oracle.attention_forward(host["q"], host["k"], host["v"], True, w.scale, heads=heads, rows=rows,
+                                              workers=WORKERS, block_mask=bm)
+    o_h, lse_h = f64(o), f64(lse)
+    for b, h in heads:
+        assert_o_bf16(o_h[b, h, rows], o_ref[b, h, rows], f"head {(b, h)}")
+        assert np.abs(lse_h[b, h, rows] - lse_ref[b, h, rows]).max() <= 1e-2
+    o_err = max(np.abs(o_h[b, h, rows] - o_ref[b, h, rows]).max() for b, h in heads)
+    groups = [(0, 6), (1, 11)]
+    dq_r, dk_r, dv_r = oracle.attention_backward(host["q"], host["k"], host["v"], host["do"], True, w.scale,
+                                                 groups=groups, workers=WORKERS, block_mask=bm)
+    e = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for b, hk in groups:
+        e["dq"] = max(e["dq"], rel_l2(f64(dq[b, hk]), dq_r[b, hk]))
+        e["dk"] = max(e["dk"], rel_l2(f64(dk[b, hk]), dk_r[b, hk]))
+        e["dv"] = max(e["dv"], rel_l2(f64(dv[b, hk]), dv_r[b, hk]))
+    print(f"\n[parity] blocksparse_n16384_d128: O max-abs {o_err:.3g} over {len(heads)} heads x {len(rows)} rows; "
+          f"rel-L2 dQ {e['dq']:.3g} dK {e['dk']:.3g} dV {e['dv']:.3g}")
+    assert max(e.values()) <= 1e-2

@@ -43,3 +43,15 @@ def test_visible_pairs_closed_forms():
             if n > w:   # causal: rows i >= w see w + 1 keys, rows i < w see i + 1
                 assert measure.visible_pairs(n, True, w) == n * (w + 1) - w * (w + 1) // 2
                 assert measure.visible_pairs(n, False, w) == 2 * measure.visible_pairs(n, True, w) - n
+
+
+def test_layout_pairs_closed_forms():
+    import numpy as np
+    from exact_io_aware_20_amd import measure
+    for n in (64, 130, 300):
+        nb = -(-n // 64)
+        ones = np.ones((nb, nb), bool)
+        assert measure.layout_pairs(n, ones, False) == n * n
+        assert measure.layout_pairs(n, ones, True) == n * (n + 1) // 2
+        assert measure.layout_pairs(n, np.eye(nb, dtype=bool), False) == sum(min(64, n - 64 * i) ** 2 for i in range(nb))
+        assert measure.layout_pairs(n, np.zeros((nb, nb), bool), True) == 0
