@@ -22,7 +22,8 @@
 //     measured slower than four.  Inside a split the per-tile
 //     steps are those of the full-sequence forward: S^T = K Q^T on the matrix
 //     cores, the lazily rescaled online softmax, O^T += V^T P^T.
-//   * Each split writes its normalised partial output and its base-2 log-sum-exp;
+//   * Each split writes its normalised partial output and its base-2 log-sum-exp (a
+//     split with no key of its sequence writes only LSE = -inf, and is skipped);
 //     a merge kernel combines the splits of a row with weights 2^(lse_s - lse),
 //     the online softmax's rescaling applied to whole partial results (lecture
 //     summary, "推导 FlashAttention 的在线 softmax").  With a single split the split
@@ -99,6 +100,16 @@ void fa_decode_split_kernel(DecodeParams p) {
     const uint16_t* Vp = (const uint16_t*)p.v;
     const uint16_t* Qr = (const uint16_t*)p.q + qrow * D;
 
+    const int ntiles = (Nk + kDecodeTile - 1) / kDecodeTile;
+    const int t0 = split * p.tiles_per_split;
+    const int t1 = min(ntiles, t0 + p.tiles_per_split);
+    if (t0 >= t1 && p.nsplit > 1) {
+        // a split past this sequence's end (paged calls with mixed lengths): it sees
+        // no key, so it records LSE = -inf only and the merge never reads its O
+        if (live && hh == 0) p.part_lse[(size_t)split * p.B * p.Hq * Nq + qrow] = kNegInf;
+        return;
+    }
+
     u32x4 qf[D / 16];
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) qf[c] = live ? ld_global16(Qr + 16 * c + 8 * hh) : zero_u4();
@@ -109,9 +120,6 @@ void fa_decode_split_kernel(DecodeParams p) {
     float m_ref = kNegInf, l_part = 0.f;
     const float sl2 = p.scale_log2;
 
-    const int ntiles = (Nk + kDecodeTile - 1) / kDecodeTile;
-    const int t0 = split * p.tiles_per_split;
-    const int t1 = min(ntiles, t0 + p.tiles_per_split);
     // Tile t holds the 64 keys starting at kbase(t), read from element offset
     // tile_off(t) of the K and V arrays.  Contiguous cache: a ragged last tile is read
     // as the last 64 keys of the cache, its keys below 64 t (already in tile t-1)
@@ -255,14 +263,16 @@ __global__ __launch_bounds__(256) void fa_decode_merge_kernel(DecodeParams p) {
 #pragma unroll 4
     for (int s = wave; s < ns; s += 4) {
         const float w = fast_exp2(p.part_lse[(size_t)s * rows + row] - M);   // -inf -> 0
-        const float* src = p.part_o + ((size_t)s * rows + row) * D + lane * E;
         wsum += w;
-        if (E == 2) {
-            const float2 x = *(const float2*)src;
-            acc[0] += w * x.x;
-            acc[E - 1] += w * x.y;
-        } else {
-            acc[0] += w * src[0];
+        if (w > 0.f) {   // a split that saw no key wrote no O
+            const float* src = p.part_o + ((size_t)s * rows + row) * D + lane * E;
+            if (E == 2) {
+                const float2 x = *(const float2*)src;
+                acc[0] += w * x.x;
+                acc[E - 1] += w * x.y;
+            } else {
+                acc[0] += w * src[0];
+            }
         }
     }
 #pragma unroll
