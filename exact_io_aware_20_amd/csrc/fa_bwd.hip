@@ -25,6 +25,9 @@
 //     LSE, D in registers) and streams K/V tiles like the forward; S^T = K Q^T
 //     keeps each lane on one query, so LSE and D are lane-local, and the K^T
 //     operand of dQ^T += K^T dS^T is read transposed from the natural K tile.
+//   * Masks: tile ranges and mask tests follow the visible band as in the forward
+//     (causal, full, sliding window); a block-sparse layout switches both kernels to
+//     compacted lists of the tiles their blocks see (SPARSE instantiations).
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 

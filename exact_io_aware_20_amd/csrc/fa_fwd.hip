@@ -25,6 +25,10 @@
 //     grows by more than 2^8 (kRescaleLog2): the quotient O = sum p v / sum p is
 //     the same for any reference, p stays <= 256, and the O rescale, which costs
 //     d/64 multiplies per score, is skipped on almost every tile.
+//   * Masks: every tile bound and mask test is written through the visible band
+//     (key j visible to query i iff i - wl <= j <= i + wr), so the causal, full and
+//     sliding-window forms share one kernel (the window form in its own
+//     instantiation); block-sparse layouts use the list-driven kernel further down.
 #include "fa_common.hpp"
 #include "fa_fwd_tile.hpp"
 #include "fa_launch.hpp"
