@@ -234,9 +234,9 @@ void fa_fwd_bf16_kernel(FwdParams p) {
 // The workgroup's 256 rows are four 64-row blocks of the layout; wave 0 compacts the
 // key tiles that any of them sees (layout bit set, and not after the block under the
 // causal rule) into an LDS list, tagged with which blocks see each, and the workgroup
-// walks that list with the per-tile steps above: K/V double-buffered, one barrier per
-// tile, and a wave computes only the tiles its own block sees.  A row that sees no key
-// gets O = 0 and LSE = -inf.
+// walks that list with the per-tile steps above, pipelined by one entry like the dense
+// kernel (K/V double-buffered, one barrier per entry); a wave computes only the tiles
+// its own block sees.  A row that sees no key gets O = 0 and LSE = -inf.
 // ---------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(FwdCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -304,27 +304,50 @@ void fa_fwd_sparse_kernel(FwdParams p) {
     TileDma<D, 1, C::WAVES> vdma;
     kdma.init(wave, lane);
     vdma.init(wave, lane);
-    auto load_tile = [&](int e) {
-        const int t = (int)(list[e] & kSparseTileMask);
-        kdma.issue(Kh + (size_t)t * C::BC * D, N - t * C::BC, kbuf + (e & 1) * KB, wave);
-        vdma.issue(Vh + (size_t)t * C::BC * D, N - t * C::BC, vbuf + (e & 1) * VB, wave);
+    auto tile = [&](int e) { return (int)(list[e] & kSparseTileMask); };
+    auto sees = [&](int e) { return ((list[e] >> wbit) & 1u) && qw0 < N; };
+    auto issue_k = [&](int e, uint16_t* buf) {
+        const int t = tile(e);
+        kdma.issue(Kh + (size_t)t * C::BC * D, N - t * C::BC, buf, wave);
     };
-    if (cnt > 0) load_tile(0);
-    for (int e = 0; e < cnt; ++e) {
+    auto issue_v = [&](int e, uint16_t* buf) {
+        const int t = tile(e);
+        vdma.issue(Vh + (size_t)t * C::BC * D, N - t * C::BC, buf, wave);
+    };
+
+    // Software-pipelined like the dense kernel, over list entries: step e forms the
+    // scores of entry e+1 (if this wave's block sees it) while it runs the softmax
+    // and P.V of entry e; LDS holds K(e+1) and V(e) during step e, and the loads of
+    // K(e+2) and V(e+1) fill the other halves of the two double buffers.
+    f32x16 sa[2], sb[2];
+    if (cnt > 0) {
+        issue_k(0, kbuf);
+        issue_v(0, vbuf);
         __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();                       // tile e landed; the other buffers are free
-        if (e + 1 < cnt) load_tile(e + 1);
-        const uint32_t ent = list[e];
-        const int k0 = (int)(ent & kSparseTileMask) * C::BC;
-        if (((ent >> wbit) & 1u) && qw0 < N) {
-            f32x16 sc[2];
-            fwd_scores<D>(kbuf + (e & 1) * KB, qf, sc, l32, hh);
-            if (k0 + C::BC - 1 > qw0 + wr || k0 + C::BC > N) fwd_mask<false>(sc, k0, 0, min(q + wr, N - 1), hh);
-            fwd_rescale<D>(sc, o, m_ref, l_part, sl2);
+        __syncthreads();
+        if (sees(0)) fwd_scores<D>(kbuf, qf, sa, l32, hh);
+        if (1 < cnt) issue_k(1, kbuf + KB);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+    auto step = [&](int e, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+        if (e + 2 < cnt) issue_k(e + 2, kbuf + (e & 1) * KB);
+        if (e + 1 < cnt) issue_v(e + 1, vbuf + ((e + 1) & 1) * VB);
+        if (e + 1 < cnt && sees(e + 1)) fwd_scores<D>(kbuf + ((e + 1) & 1) * KB, qf, nxt, l32, hh);
+        if (sees(e)) {
+            const int k0 = tile(e) * C::BC;
+            if (k0 + C::BC - 1 > qw0 + wr || k0 + C::BC > N) fwd_mask<false>(cur, k0, 0, min(q + wr, N - 1), hh);
+            fwd_rescale<D>(cur, o, m_ref, l_part, sl2);
             u32x4 pf[2][2];
-            fwd_probs(sc, m_ref, sl2, pf, l_part);
+            fwd_probs(cur, m_ref, sl2, pf, l_part);
             fwd_pv<D>(vbuf + (e & 1) * VB, pf, o, lane);
         }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+    for (int e = 0; e < cnt; e += 2) {
+        step(e, sa, sb);
+        if (e + 1 < cnt) step(e + 1, sb, sa);
     }
 
     const float lt = l_part + __shfl_xor(l_part, 32);
