@@ -7,7 +7,8 @@ Bars (as for the dense bf16 path): |O - O_ref| <= 1e-2 + half a bf16 ulp,
 relative L2 <= 1e-2 for dQ, dK and dV.  Small cases use seeded random layouts (with
 empty block rows), ragged lengths, grouped-query heads, both head sizes and both
 mask settings; the local + global workload is checked at full size on sampled rows
-and two KV groups.
+and two KV groups; the largest layout (2048 x 2048 blocks, N = 131072) on sampled
+forward rows and two column sums of the gradients that hold at any size.
 """
 import math
 import sys
@@ -131,3 +132,36 @@ def test_blocksparse_workload_full_size():
     print(f"\n[parity] blocksparse_n16384_d128: O max-abs {o_err:.3g} over {len(heads)} heads x {len(rows)} rows; "
           f"rel-L2 dQ {e['dq']:.3g} dK {e['dk']:.3g} dV {e['dv']:.3g}")
     assert max(e.values()) <= 1e-2
+
+
+def test_blocksparse_largest_layout():
+    # N = 131072: a 2048 x 2048 layout, the most the per-workgroup list holds.  The
+    # forward is checked on sampled rows; the backward through two sums that hold at
+    # any size: sum_j dV_j = sum_i dO_i over rows that see a key (each such row's P
+    # sums to 1), and sum_j dK_j = scale sum_i q_i sum_j dS_ij = 0.
+    B, Hq, Hkv, N, d = 1, 1, 1, 131072, 64
+    host, g = make(B, Hq, Hkv, N, d, seed=16700, with_do=True)
+    lay = inputs.random_layout(N, 0.01, 16701)
+    lay[torch.arange(lay.shape[0]), torch.arange(lay.shape[0])] = 1     # every row sees its own block
+    scale = 1.0 / math.sqrt(d)
+    o, lse = api.forward(g["q"], g["k"], g["v"], True, scale, block_mask=lay.to(dev()))
+    dq, dk, dv = api.backward(g["q"], g["k"], g["v"], o, g["do"], lse, True, scale, block_mask=lay.to(dev()))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(16702)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(N - 64, N), rng.choice(N, 256, replace=False)]))
+    o_ref, lse_ref = oracle.attention_forward(host["q"], host["k"], host["v"], True, scale, rows=rows,
+                                              block_mask=lay.numpy().astype(bool))
+    assert_o_bf16(f64(o)[0, 0, rows], o_ref[0, 0, rows], "largest layout")
+    assert np.abs(f64(lse)[0, 0, rows] - lse_ref[0, 0, rows]).max() <= 1e-2
+    do_sum = host["do"].double().sum(dim=2)[0, 0].numpy()
+    dv_sum = dv.double().sum(dim=2)[0, 0].cpu().numpy()
+    dk_sum = dk.double().sum(dim=2)[0, 0].cpu().numpy()
+    # each bound is 0.1% of the column's absolute sum, well above the rounding of the
+    # bf16 outputs and of the D_i = dO_i . O_i the kernels take from the rounded O
+    nv = np.abs(f64(dv)[0, 0]).sum(axis=0)
+    nk = np.abs(f64(dk)[0, 0]).sum(axis=0)
+    ev, ek = np.abs(dv_sum - do_sum), np.abs(dk_sum)
+    print(f"\n[parity] blocksparse N=131072: |sum dV - sum dO| / sum|dV| {(ev / nv).max():.3e}, "
+          f"|sum dK| / sum|dK| {(ek / nk).max():.3e}")
+    assert (ev <= 1e-3 * nv).all() and (ek <= 1e-3 * nk).all()
+    assert np.isfinite(f64(dq)).all()

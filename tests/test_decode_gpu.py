@@ -6,7 +6,8 @@ Bars (the same as the full-sequence bf16 forward, element by element):
 |O - O_ref| <= 1e-2 + half a bf16 ulp of O_ref and |LSE - LSE_ref| <= 1e-2.
 Small shapes cover caches shorter than one tile, ragged tails, one and several key
 splits, one to four 32-row blocks of packed (head, query) rows, both head sizes and
-both mask settings; the two decode workloads are checked whole at full size.
+both mask settings; the two decode workloads are checked whole at full size, and a
+2^20-token cache (about a thousand splits merged per row) whole.
 """
 import math
 import sys
@@ -120,4 +121,17 @@ def test_decode_workload_full_size(name):
     err = assert_o_bf16(f64(o), o_ref, name)
     lerr = float(np.abs(f64(lse) - lse_ref).max())
     print(f"[parity] {name} O max-abs {err:.3e} LSE max-abs {lerr:.3e}")
+    assert lerr <= 1e-2
+
+
+def test_decode_million_token_cache():
+    # one sequence of 2^20 cached tokens: about 1024 key splits merged per row
+    shape = (1, 8, 1, 2, 1 << 20, 128)
+    host, g = make(*shape, seed=12100)
+    o, lse = api.decode_forward(g["q"], g["k"], g["v"], True, 0.088)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_forward(host["q"], host["k"], host["v"], True, 0.088)
+    err = assert_o_bf16(f64(o), o_ref, "1M cache")
+    lerr = float(np.abs(f64(lse) - lse_ref).max())
+    print(f"[parity] decode 2^20-token cache: O max-abs {err:.3e} LSE max-abs {lerr:.3e}")
     assert lerr <= 1e-2
