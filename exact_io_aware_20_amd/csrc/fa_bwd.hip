@@ -15,7 +15,7 @@
 //     workspace that the other two kernels read.
 //   * dK/dV kernel: a workgroup owns 128 keys of one KV head, 32 per pair of waves
 //     (one forms S, P and dV, its partner dP, dS and dK one item later, P handed
-//     over through LDS), streaming 64-row tiles of Q and dO of every query head in
+//     over through LDS in bf16), streaming 64-row tiles of Q and dO of every query head in
 //     the group through LDS by direct loads.  S = Q K^T is formed with the query on
 //     the C rows, so P and dS feed the dV and dK contractions straight from
 //     registers; the Q^T and dO^T operands of those contractions come from the same
@@ -82,17 +82,38 @@ struct DkdvCfg {
     static constexpr int NAT = SwzTile<D, 1>::ELEMS;    // natural Q or dO tile (bf16 elements)
     static constexpr int STAGE = 2 * NAT + 2 * BQ * 2;  // Q, dO, then LSE2 and D (fp32, BQ each)
     static constexpr int NSTAGE = 3;                    // items it+1 (loading), it, it-1
-    static constexpr int PBUF = 4 * 32 * 64 * 2;        // fp32 P of one item: 4 pairs x 32 x 64 lanes (bf16 units)
+    static constexpr int PBUF = 2 * 4 * 32 * 64;        // bf16 P of two items: 2 x 4 pairs x 32 keys x 64 queries
+};
+
+// Element offsets of the row fragments (row l32, chunk 2k + hh) of a MODE 1 tile;
+// query half qb adds 32 qb rows, a constant.
+template <int D>
+struct RowOffsets {
+    uint32_t off[D / 16];
+    __device__ __forceinline__ void init(int l32, int hh) {
+        using NT = SwzTile<D, 1>;
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) off[k] = (uint32_t)NT::at(l32, 2 * k + hh);
+    }
+};
+
+// row fragments of the MODE 1 tile at LDS byte address `base`
+template <int D>
+struct RowAddr {
+    uint32_t a[D / 16];
+    __device__ __forceinline__ RowAddr(const RowOffsets<D>& o, uint32_t base) {
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) a[k] = opaque(base + 2 * o.off[k]);
+    }
 };
 
 // C[q][key] = sum_d A[q][d] B[key][d] for query half qb (32 rows) of a natural
 // tile and the wave's 32 keys (B fragments in registers): queries on the C rows.
 template <int D>
-__device__ __forceinline__ f32x16 qk_half(const uint16_t* nat, const u32x4 (&bf)[D / 16], int qb, int l32, int hh) {
-    using NT = SwzTile<D, 1>;
+__device__ __forceinline__ f32x16 qk_half(const RowAddr<D>& ra, const u32x4 (&bf)[D / 16], int qb) {
     f32x16 c = zero16();
 #pragma unroll
-    for (int k = 0; k < D / 16; ++k) c = mfma32x32x16(lds16(nat + NT::at(32 * qb + l32, 2 * k + hh)), bf[k], c);
+    for (int k = 0; k < D / 16; ++k) c = mfma32x32x16(lds16_a(ra.a[k] + 2 * 32 * qb * D), bf[k], c);
     return c;
 }
 
@@ -125,32 +146,29 @@ __device__ __forceinline__ void pack_half(const f32x16& x, u32x4 (&bf)[2]) {
 }
 
 // acc^T += T^T X over one query half: A operand read transposed from the natural
-// tile `tt` (Q or dO), B operand the packed half `bf`.
+// tile (Q or dO) that `ta` addresses, B operand the packed half `bf`.
 template <int D>
-__device__ __forceinline__ void acc_half(const uint16_t* tt, const u32x4 (&bf)[2], f32x16 (&acc)[D / 32], int qb,
-                                         int lane) {
+__device__ __forceinline__ void acc_half(const TrAddr<D>& ta, const u32x4 (&bf)[2], f32x16 (&acc)[D / 32], int qb) {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-            acc[db] = mfma32x32x16(tr_frag<D>(tt, db, 32 * qb + 16 * h2, lane), bf[h2], acc[db]);
+        for (int db = 0; db < D / 32; ++db) acc[db] = mfma32x32x16(ta.frag(db, 32 * qb + 16 * h2), bf[h2], acc[db]);
 }
 
 // dK/dV kernel.  A workgroup owns 128 keys of one KV head.  Wave w < 4 ("P/dV")
 // and wave w + 4 ("dS/dK") own keys 32w .. 32w+31; the first computes S = Q K^T,
-// P = 2^(S*sl2 - LSE2) and dV^T += dO^T P for item it and hands P (fp32) to its
-// partner through LDS; the partner, one item behind, computes dP = dO V^T,
-// dS = P (dP - D) and dK^T += Q^T dS for item it-1.  S and the exponentials are
-// thus formed once per item.  Items are (query head of the group, 64-row query
-// tile); their Q and dO tiles and LSE2/D vectors sit in stage it%3 of LDS, filled
-// by direct loads.  Iteration it:
-//   barrier A: item it landed; items it-1 (still read by dS/dK) and it stay, the
-//              stage of item it-2 is free and receives item it+1's loads;
-//   P/dV: S, mask, P of item it;        dS/dK: P(it-1) from LDS, dP of item it-1;
-//   barrier B (P(it-1) has been read);
-//   P/dV: P(it) to LDS, dV MFMAs;       dS/dK: dS and dK MFMAs of item it-1.
-// In each half one wave of a SIMD pair runs exponentials or dS while the other
-// runs matrix work.
+// P = 2^(S*sl2 - LSE2) and dV^T += dO^T P for item it and hands P to its partner
+// through LDS, as the bf16 fragments the dV product uses; the partner, one item
+// behind, computes dP = dO V^T, dS = P (dP - D) and dK^T += Q^T dS for item it-1.
+// S and the exponentials are thus formed once per item.  Items are (query head of
+// the group, 64-row query tile); their Q and dO tiles and LSE2/D vectors sit in
+// stage it%3 of LDS, filled by direct loads, and P of item it in P slot it%2.  One
+// barrier per iteration it: item it has landed and P(it-1) has been written; the
+// stage of item it-2 is free and receives item it+1's loads, and P slot (it+1)%2
+// was last read (P(it-1)) before this barrier.  Between barriers the P/dV wave
+// runs S, mask, P, P to LDS and the dV MFMAs of item it while its partner runs P
+// from LDS, dP, dS and the dK MFMAs of item it-1, so one wave of a SIMD pair runs
+// exponentials or dS while the other runs matrix work.
 template <int D, bool PV, bool SPARSE>
 __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, const uint32_t* list, int list_n,
                                           int wave, int lane) {
@@ -188,10 +206,15 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, co
     const uint32_t wbit = 20u + (uint32_t)((wave & 3) >> 1);
     const int nitems = G * per_head;
     const float sl2 = p.scale_log2;
-    float* pbuf = (float*)(smem + C::NSTAGE * C::STAGE) + (wave & 3) * 32 * 64;   // this pair's P slots
+    // this pair's P slots (one per item parity): 64 lanes x 4 packed fragments each
+    uint32_t* pbuf = (uint32_t*)(smem + C::NSTAGE * C::STAGE) + (wave & 3) * 64 * 16;
 
     TileDma<D, 1, C::WAVES> dma;
     dma.init(wave, lane);
+    RowOffsets<D> ro;
+    ro.init(l32, hh);
+    TrOffsets<D> to;
+    to.init(lane);
     auto item_q0 = [&](int it) {
         if constexpr (SPARSE) return (int)(list[it % per_head] & kSparseTileMask) * C::BQ;
         return (qt_start + it % per_head) * C::BQ;
@@ -227,14 +250,19 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, co
         if (it + 1 < nitems) issue_item(it + 1);
         f32x16 x[2];                                                   // P (P/dV) or dP (dS/dK)
         f32x16 pp[2];                                                  // dS/dK: P of its item
-        // each half's critical wave (P/dV before barrier B, dS/dK after) issues first
+        // the wave whose result the other waits on issues first: P/dV while it forms
+        // P, dS/dK while it forms dS and dK
         __builtin_amdgcn_s_setprio(PV ? 2 : 0);
         if (act) {
             if constexpr (PV) {
                 const bool mask = q0 < kw0 + 31 - wr || q0 + C::BQ > N || q0 + C::BQ - 1 > kw0 + wl;
+                {
+                    const RowAddr<D> ra(ro, lds_addr(st));
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb) x[qb] = qk_half<D>(ra, bfr, qb);
+                }
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
-                    x[qb] = qk_half<D>(st, bfr, qb, l32, hh);
                     if (mask) mask_half(x[qb], q0 + 32 * qb + 4 * hh, key, N, wl, wr);
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
@@ -245,35 +273,44 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, co
                     }
                 }
             } else {
+                const uint32_t* pb = pbuf + (mine & 1) * 4 * 64 * 16;
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const f32x4 v = *(const f32x4*)(pbuf + (4 * qb + g) * 4 * 64 + 4 * lane);
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const u32x4 v = *(const u32x4*)(pb + ((2 * qb + h2) * 64 + lane) * 4);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) pp[qb][4 * g + i] = v[i];
+                        for (int j = 0; j < 4; ++j) {
+                            // inverse of pack_half: word j of fragment h2 holds registers
+                            // r and r + 1, r = 4 (2 h2 + j/2) + 2 (j%2)
+                            const int r = 4 * (2 * h2 + (j >> 1)) + 2 * (j & 1);
+                            pp[qb][r] = bf16_lo(v[j]);
+                            pp[qb][r + 1] = bf16_hi(v[j]);
+                        }
                     }
+                {
+                    const RowAddr<D> ra(ro, lds_addr(st + C::NAT));
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) x[qb] = qk_half<D>(st + C::NAT, bfr, qb, l32, hh);
+                    for (int qb = 0; qb < 2; ++qb) x[qb] = qk_half<D>(ra, bfr, qb);
+                }
             }
         }
-        __syncthreads();                                               // B
         __builtin_amdgcn_s_setprio(PV ? 0 : 2);
         if (act) {
             if constexpr (PV) {
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        *(f32x4*)(pbuf + (4 * qb + g) * 4 * 64 + 4 * lane) =
-                            f32x4{x[qb][4 * g], x[qb][4 * g + 1], x[qb][4 * g + 2], x[qb][4 * g + 3]};
+                u32x4 bf[2][2];
+                uint32_t* pb = pbuf + (mine & 1) * 4 * 64 * 16;
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
-                    u32x4 bf[2];
-                    pack_half(x[qb], bf);
-                    acc_half<D>(st + C::NAT, bf, acc, qb, lane);       // dV^T += dO^T P
+                    pack_half(x[qb], bf[qb]);
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) *(u32x4*)(pb + ((2 * qb + h2) * 64 + lane) * 4) = bf[qb][h2];
                 }
+                const TrAddr<D> ta(to, lds_addr(st + C::NAT));
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) acc_half<D>(ta, bf[qb], acc, qb);   // dV^T += dO^T P
             } else {
+                u32x4 bf[2][2];
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
@@ -282,10 +319,11 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, co
 #pragma unroll
                         for (int i = 0; i < 4; ++i) x[qb][4 * g + i] = pp[qb][4 * g + i] * (x[qb][4 * g + i] - Dd[i]);
                     }
-                    u32x4 bf[2];
-                    pack_half(x[qb], bf);
-                    acc_half<D>(st, bf, acc, qb, lane);                // dK^T += Q^T dS
+                    pack_half(x[qb], bf[qb]);
                 }
+                const TrAddr<D> ta(to, lds_addr(st));
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) acc_half<D>(ta, bf[qb], acc, qb);   // dK^T += Q^T dS
             }
         }
     }

@@ -202,6 +202,59 @@ __device__ __forceinline__ u32x4 tr_frag(const uint16_t* tile, int db, int kk, i
     return cat(lo, hi);
 }
 
+// Loop-hoisted LDS addressing.  Both swizzles depend on the row mod 16 only, so a
+// fragment whose rows start at a multiple of 16 is a fixed per-lane offset plus a
+// constant.  A kernel keeps the per-lane offsets, adds the current stage's LDS base
+// once per tile, and hides that sum from the optimiser (opaque), so each constant
+// stays an immediate of the read; without this the compiler hoisted one register per
+// (fragment, constant) pair and re-added the stage base before every read.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+__device__ __forceinline__ u32x2 tr_read_a(uint32_t a) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)a));
+}
+__device__ __forceinline__ u32x4 lds16_a(uint32_t a) {
+    return *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)a;
+}
+
+// Element offsets of the two tr_frag reads of column block db at kk = 0 (MODE 1 tile).
+template <int D>
+struct TrOffsets {
+    uint32_t off[D / 32][2];
+    __device__ __forceinline__ void init(int lane) {
+        using S = SwzTile<D, 1>;
+        const int g = lane >> 4, m = lane & 15;
+        const int row = 4 * (g >> 1) + (m >> 2);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const int col = 32 * db + 16 * (g & 1) + 4 * (m & 3);
+            off[db][0] = (uint32_t)(S::at(row, col >> 3) + (col & 7));
+            off[db][1] = (uint32_t)(S::at(row + 8, col >> 3) + (col & 7));
+        }
+    }
+};
+
+// tr_frag of the MODE 1 tile at LDS byte address `base`, for kk a multiple of 16
+template <int D>
+struct TrAddr {
+    uint32_t a[D / 32][2];
+    __device__ __forceinline__ TrAddr(const TrOffsets<D>& o, uint32_t base) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            a[db][0] = opaque(base + 2 * o.off[db][0]);
+            a[db][1] = opaque(base + 2 * o.off[db][1]);
+        }
+    }
+    __device__ __forceinline__ u32x4 frag(int db, int kk) const {
+        return cat(tr_read_a(a[db][0] + 2 * kk * D), tr_read_a(a[db][1] + 2 * kk * D));
+    }
+};
+
 // ---------------------------------------------------------------------------------
 // Block-sparse layouts: a 0/1 byte matrix over 64 x 64 blocks of (query, key)
 // positions, nb x nb with nb = ceil(N / 64), shared by every (batch, head).  A
