@@ -187,8 +187,19 @@ struct TileDma {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// The transposing read goes through a helper whose pointer parameter is restrict:
+// once inlined, the read carries alias-scope metadata.  Without it the compiler has
+// no alias information for the read and waits for every direct global->LDS load
+// still in flight (s_waitcnt vmcnt(0)) before it, which would stall each tile step
+// on the prefetch of the next tiles.  Every kernel here waits for its direct loads
+// explicitly (s_waitcnt, then a workgroup barrier) before any wave reads the LDS
+// they fill, and never reads a buffer while a load into it is in flight, so the
+// implicit wait is not needed for correctness.
+__device__ __forceinline__ s16x4 tr_read_lds(const lds_s16x4* __restrict__ p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+}
 __device__ __forceinline__ u32x2 tr_read(const uint16_t* p) {
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
+    return __builtin_bit_cast(u32x2, tr_read_lds((const lds_s16x4*)(p)));
 }
 
 template <int D>
@@ -216,7 +227,7 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
     return x;
 }
 __device__ __forceinline__ u32x2 tr_read_a(uint32_t a) {
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)a));
+    return __builtin_bit_cast(u32x2, tr_read_lds((const lds_s16x4*)(uintptr_t)a));
 }
 __device__ __forceinline__ u32x4 lds16_a(uint32_t a) {
     return *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)a;
