@@ -226,12 +226,19 @@ void fa_decode_split_kernel(DecodeParams p) {
 // maximum M and weights w_s = 2^(lse_s - M); O = sum_s w_s O_s / sum_s w_s and
 // LSE = (M + log2 sum_s w_s) ln 2.  Wave w sums the splits s = w, w+4, ...; lane l
 // holds elements l*D/64 .. of the row.
+// One workgroup per query row.  The splits' base-2 LSEs are staged in LDS and turned
+// into weights 2^(lse_s - M), M their maximum; then thread t adds the weighted
+// partial outputs of splits t / (D/4), t / (D/4) + GR, ... for its four elements
+// d = 4 (t % (D/4)) .. +3 (GR = 256 / (D/4) split groups).  The loop is unrolled so
+// that a thread's loads are in flight together, and the split groups are summed
+// through LDS at the end.  nsplit <= kDecodeTargetWgs (checked by the launcher).
 template <int D>
 __global__ __launch_bounds__(256) void fa_decode_merge_kernel(DecodeParams p) {
-    constexpr int E = D / 64;   // elements per lane
-    __shared__ float red[4][D];
-    __shared__ float wred[4];
-    __shared__ float mred[4];
+    constexpr int C4 = D / 4;        // float4 chunks of a row
+    constexpr int GR = 256 / C4;     // split groups
+    __shared__ float wts[kDecodeTargetWgs];
+    __shared__ f32x4 red[GR][C4];
+    __shared__ float rmax[4], rsum[4];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -240,58 +247,56 @@ __global__ __launch_bounds__(256) void fa_decode_merge_kernel(DecodeParams p) {
     const int ns = p.nsplit;
 
     float mx = kNegInf;
-    for (int s = tid; s < ns; s += 256) mx = fmaxf(mx, p.part_lse[(size_t)s * rows + row]);
+    for (int s = tid; s < ns; s += 256) {
+        const float l = p.part_lse[(size_t)s * rows + row];
+        wts[s] = l;
+        mx = fmaxf(mx, l);
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if (lane == 0) mred[wave] = mx;
+    if (lane == 0) rmax[wave] = mx;
     __syncthreads();
-    const float M = fmaxf(fmaxf(mred[0], mred[1]), fmaxf(mred[2], mred[3]));
+    const float M = fmaxf(fmaxf(rmax[0], rmax[1]), fmaxf(rmax[2], rmax[3]));
     if (M == kNegInf) {   // no split saw a key (a paged sequence shorter than its queries)
-        if (wave == 0) {
-            uint16_t* Or = (uint16_t*)p.o + row * D + lane * E;
-#pragma unroll
-            for (int e = 0; e < E; ++e) Or[e] = 0;
-            if (lane == 0) p.lse[row] = kNegInf;
+        if (tid < C4) {
+            uint16_t* Or = (uint16_t*)p.o + row * D + 4 * tid;
+            *(u32x2*)Or = u32x2{0u, 0u};
         }
+        if (tid == 0) p.lse[row] = kNegInf;
         return;
     }
-
-    float acc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    float wsum = 0.f;
-#pragma unroll 4
-    for (int s = wave; s < ns; s += 4) {
-        const float w = fast_exp2(p.part_lse[(size_t)s * rows + row] - M);   // -inf -> 0
-        wsum += w;
-        if (w > 0.f) {   // a split that saw no key wrote no O
-            const float* src = p.part_o + ((size_t)s * rows + row) * D + lane * E;
-            if (E == 2) {
-                const float2 x = *(const float2*)src;
-                acc[0] += w * x.x;
-                acc[E - 1] += w * x.y;
-            } else {
-                acc[0] += w * src[0];
-            }
-        }
+    float ws = 0.f;
+    for (int s = tid; s < ns; s += 256) {
+        const float w = fast_exp2(wts[s] - M);   // -inf -> 0
+        wts[s] = w;
+        ws += w;
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) red[wave][lane * E + e] = acc[e];
-    if (lane == 0) wred[wave] = wsum;
+    for (int off = 32; off >= 1; off >>= 1) ws += __shfl_xor(ws, off);
+    if (lane == 0) rsum[wave] = ws;
     __syncthreads();
-    if (wave == 0) {
-        const float wt = wred[0] + wred[1] + wred[2] + wred[3];
-        const float inv = 1.0f / wt;
-        uint16_t* Or = (uint16_t*)p.o + row * D + lane * E;
-        float x[E];
+
+    const int g = tid / C4, c = tid % C4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int s = g; s < ns; s += GR) {
+        const float w = wts[s];
+        if (w > 0.f) {   // a split that saw no key wrote no O
+            const f32x4 x = *(const f32x4*)(p.part_o + ((size_t)s * rows + row) * D + 4 * c);
+            acc += w * x;
+        }
+    }
+    red[g][c] = acc;
+    __syncthreads();
+    if (tid < C4) {
+        f32x4 x = red[0][tid];
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-            x[e] = (red[0][lane * E + e] + red[1][lane * E + e] + red[2][lane * E + e] + red[3][lane * E + e]) * inv;
-        if (E == 2)
-            *(uint32_t*)Or = pack_bf16(x[0], x[E - 1]);
-        else
-            Or[0] = (uint16_t)(pack_bf16(x[0], 0.f) & 0xffffu);
-        if (lane == 0) p.lse[row] = (M + __log2f(wt)) * kLn2;
+        for (int j = 1; j < GR; ++j) x += red[j][tid];
+        const float wt = rsum[0] + rsum[1] + rsum[2] + rsum[3];
+        x *= 1.0f / wt;
+        uint16_t* Or = (uint16_t*)p.o + row * D + 4 * tid;
+        *(u32x2*)Or = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+        if (tid == 0) p.lse[row] = (M + __log2f(wt)) * kLn2;
     }
 }
 
@@ -326,6 +331,7 @@ static hipError_t launch_decode_d(const DecodeParams& p, int steps, bool paged, 
         if (e != hipSuccess) return e;
     }
     if ((steps & kDecodeMerge) && p.nsplit > 1) {
+        if (p.nsplit > kDecodeTargetWgs) return hipErrorInvalidValue;   // the plan never makes more
         const long long rows = (long long)p.B * p.Hq * p.Nq;
         hipLaunchKernelGGL((fa_decode_merge_kernel<D>), dim3((unsigned)rows), dim3(256), 0, stream, p);
         return hipGetLastError();
