@@ -3,6 +3,7 @@ that bench.py reports beside its roofline.
 
     python -m exact_io_aware_20_amd.profile_summary trace  <trace_dir> <out.md> <warmup_launches> <command>
     python -m exact_io_aware_20_amd.profile_summary traffic <fetch_dir> <write_dir> <out.md> <calib_mib> <command>
+    python -m exact_io_aware_20_amd.profile_summary mfma <pmc_dir> <out.md> <command>
 
 `trace` turns a `--kernel-trace --stats` run into a table of per-kernel launch
 counts and durations.  `traffic` reads two `--pmc` runs (FETCH_SIZE, then
@@ -11,7 +12,9 @@ launches one plain streaming kernel of known size (an elementwise negation of M 
 of fp32 into another M MiB buffer).  Each counter is scaled by the ratio of that
 kernel's true bytes to what the same counter reads for it, and the per-launch HBM
 bytes of every attention kernel are written with a digest of the kernel sources;
-bench.py uses the figure only while the sources still match the digest.
+bench.py uses the figure only while the sources still match the digest.  `mfma`
+reads a `--pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE` run and reports the share
+of SIMD cycles each attention kernel kept the matrix pipe busy.
 """
 from __future__ import annotations
 
@@ -165,12 +168,64 @@ def _write_traffic_md(t, out, command):
         f.write("\n".join(lines) + "\n")
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+
+
+def gpu_agent(pmc_dir: str) -> dict:
+    """SIMD count and XCD count of the GPU agent of a rocprofv3 run (its agent_info.csv);
+    MI355X's figures (1024 SIMDs, 8 XCDs) when the file has no GPU row."""
+    try:
+        with open(_find(pmc_dir, "agent_info.csv")) as f:
+            for r in csv.DictReader(f):
+                if int(r.get("Simd_Count", "0") or 0) > 0:
+                    return {"simds": int(r["Simd_Count"]), "xcc": max(1, int(r.get("Num_Xcc", "1") or 1))}
+    except FileNotFoundError:
+        pass
+    return {"simds": 1024, "xcc": 8}
+
+
+def mfma_busy(pmc_dir: str) -> dict:
+    """Per attention kernel: the means per dispatch of SQ_VALU_MFMA_BUSY_CYCLES (summed
+    over every SIMD) and GRBM_GUI_ACTIVE (GPU-busy cycles of the dispatch, which the
+    profiler sums over the XCDs, each having its own counter), and the share of SIMD
+    cycles the matrix pipe was busy: busy / (active / XCDs x SIMDs)."""
+    agent = gpu_agent(pmc_dir)
+    busy = counter_means(pmc_dir, MFMA_COUNTERS[0])
+    active = counter_means(pmc_dir, MFMA_COUNTERS[1])
+    out = {}
+    for k, b in busy.items():
+        if "fa_" not in k or k not in active or active[k] <= 0:
+            continue
+        cycles = active[k] / agent["xcc"]
+        out[short_name(k)] = {"mfma_busy": b, "gui_active": active[k], "frac": b / (cycles * agent["simds"])}
+    return {"agent": agent, "kernels": out}
+
+
+def _write_mfma_md(m, out, command):
+    a = m["agent"]
+    lines = [f"# MFMA busy: {os.path.splitext(os.path.basename(out))[0].replace('mfma_busy_', '')}", "",
+             "One counter run (run from the repository root; `$R` is the repository path):", "",
+             f"    {command}", "",
+             f"`frac` = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {a['xcc']} XCDs x {a['simds']} SIMDs): the "
+             "share of SIMD cycles in which the matrix pipe was busy during the kernel (means per dispatch; "
+             "the profiler sums GRBM_GUI_ACTIVE over the XCDs). It counts executed MFMAs, so for dQ it "
+             "includes the recomputed S and dP contractions, and it is measured against the clock the "
+             f"kernel ran at, not the 2.4 GHz of the published peak. Kernel sources digest: `{source_digest()}`.",
+             "", "| kernel | SQ_VALU_MFMA_BUSY_CYCLES | GRBM_GUI_ACTIVE | frac |", "|---|---|---|---|"]
+    for k, v in sorted(m["kernels"].items()):
+        lines.append(f"| {k} | {v['mfma_busy']:.4g} | {v['gui_active']:.4g} | {v['frac']:.3f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main(argv):
     if len(argv) >= 5 and argv[0] == "trace":
         skip = int(argv[3])
         _write_trace_md(trace_table(argv[1]), timed_means(argv[1], skip), skip, argv[2], argv[4])
     elif len(argv) >= 6 and argv[0] == "traffic":
         _write_traffic_md(traffic(argv[1], argv[2], int(argv[4])), argv[3], argv[5])
+    elif len(argv) >= 4 and argv[0] == "mfma":
+        _write_mfma_md(mfma_busy(argv[1]), argv[2], argv[3])
     else:
         raise SystemExit(__doc__)
 

@@ -38,3 +38,23 @@ def test_committed_traffic_needs_matching_sources(tmp_path):
 
 def test_short_name():
     assert ps.short_name("void fa::fa_bwd_dkdv_kernel<128>(fa::BwdParams)") == "fa_bwd_dkdv_kernel<128>"
+
+
+def test_mfma_busy_fraction(tmp_path):
+    fw = "void fa::fa_fwd_bf16_kernel<128, false>(fa::FwdParams)"
+    d = tmp_path / "m"
+    os.makedirs(d)
+    with open(d / "p_agent_info.csv", "w") as f:
+        f.write("Agent_Type,Simd_Count,Num_Xcc\nCPU,0,0\nGPU,1024,8\n")
+    with open(d / "p_counter_collection.csv", "w") as f:
+        f.write('"Kernel_Name","Counter_Name","Counter_Value"\n')
+        # GRBM_GUI_ACTIVE summed over 8 XCDs: 1000 cycles each; the 1024 SIMDs' matrix
+        # pipes busy 400 and 600 of them in the two dispatches
+        for busy in (1024 * 400, 1024 * 600):
+            f.write(f'"{fw}","SQ_VALU_MFMA_BUSY_CYCLES",{busy}\n')
+            f.write(f'"{fw}","GRBM_GUI_ACTIVE",8000\n')
+        f.write('"other_kernel","SQ_VALU_MFMA_BUSY_CYCLES",5\n"other_kernel","GRBM_GUI_ACTIVE",5\n')
+    m = ps.mfma_busy(str(d))
+    assert m["agent"] == {"simds": 1024, "xcc": 8}
+    assert list(m["kernels"]) == ["fa_fwd_bf16_kernel<128, false>"]
+    assert abs(m["kernels"]["fa_fwd_bf16_kernel<128, false>"]["frac"] - 0.5) < 1e-12
