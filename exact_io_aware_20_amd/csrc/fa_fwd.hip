@@ -191,16 +191,16 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         }
     };
 
-    // prologue: K(t0), V(t0) -> LDS; S(t0); K(t0+1) -> LDS (buffers by tile parity)
+    // prologue: K(t0), V(t0) and K(t0+1) -> LDS in one round trip (buffers by tile
+    // parity); S(t0); a barrier before the first step reloads K(t0)'s buffer
     const int tb = t_begin & 1;
     issue_k(t_begin, kbuf + tb * KB);
     issue_v(t_begin, vbuf + tb * VB);
+    if (t_begin + 1 < ntiles) issue_k(t_begin + 1, kbuf + (tb ^ 1) * KB);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     f32x16 sa[2], sb[2];
     if (t_begin < wave_tiles) scores_of(kbuf + tb * KB, sa);
-    if (t_begin + 1 < ntiles) issue_k(t_begin + 1, kbuf + (tb ^ 1) * KB);
-    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     // Fast step: tiles t and t+1 are fully visible to every row of the workgroup
