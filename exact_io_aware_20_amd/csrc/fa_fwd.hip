@@ -397,14 +397,13 @@ void fa_fwd_sparse_kernel(FwdParams p) {
     // and P.V of entry e; LDS holds K(e+1) and V(e) during step e, and the loads of
     // K(e+2) and V(e+1) fill the other halves of the two double buffers.
     f32x16 sa[2], sb[2];
-    if (cnt > 0) {
+    if (cnt > 0) {   // K(0), V(0) and K(1) in one round trip, as in the dense kernel
         issue_k(0, kbuf);
         issue_v(0, vbuf);
+        if (1 < cnt) issue_k(1, kbuf + KB);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (sees(0)) fwd_scores<D>(kbuf, qf, sa, l32, hh);
-        if (1 < cnt) issue_k(1, kbuf + KB);
-        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
     auto step = [&](int e, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
