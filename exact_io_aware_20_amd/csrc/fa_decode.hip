@@ -222,12 +222,10 @@ void fa_decode_split_kernel(DecodeParams p) {
     }
 }
 
-// One workgroup (4 waves) per query row: the splits' base-2 LSEs give the row's
-// maximum M and weights w_s = 2^(lse_s - M); O = sum_s w_s O_s / sum_s w_s and
-// LSE = (M + log2 sum_s w_s) ln 2.  Wave w sums the splits s = w, w+4, ...; lane l
-// holds elements l*D/64 .. of the row.
-// One workgroup per query row.  The splits' base-2 LSEs are staged in LDS and turned
-// into weights 2^(lse_s - M), M their maximum; then thread t adds the weighted
+// One workgroup per query row: the splits' base-2 LSEs give the row's maximum M and
+// weights w_s = 2^(lse_s - M); O = sum_s w_s O_s / sum_s w_s and
+// LSE = (M + log2 sum_s w_s) ln 2.  The LSEs are staged in LDS and turned into the
+// weights there; then thread t adds the weighted
 // partial outputs of splits t / (D/4), t / (D/4) + GR, ... for its four elements
 // d = 4 (t % (D/4)) .. +3 (GR = 256 / (D/4) split groups).  The loop is unrolled so
 // that a thread's loads are in flight together, and the split groups are summed

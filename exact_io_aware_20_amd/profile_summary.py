@@ -33,11 +33,19 @@ KERNEL_SOURCES = ("fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_fwd_tile.hpp"
 TRAFFIC_TAG = "traffic-json:"
 
 
+def code_text(src: str) -> str:
+    """The source with comments removed and whitespace collapsed, so that edits to
+    comments alone leave the digest (and the profiles it guards) valid."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def source_digest() -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "csrc", name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(ROOT, "csrc", name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -58,3 +58,9 @@ def test_mfma_busy_fraction(tmp_path):
     assert m["agent"] == {"simds": 1024, "xcc": 8}
     assert list(m["kernels"]) == ["fa_fwd_bf16_kernel<128, false>"]
     assert abs(m["kernels"]["fa_fwd_bf16_kernel<128, false>"]["frac"] - 0.5) < 1e-12
+
+
+def test_digest_ignores_comments_only():
+    code = "int f(int x) {\n    return x + 1;   // one more\n}\n/* block\n comment */\n"
+    assert ps.code_text(code) == ps.code_text("int f(int x) { return x + 1; }")
+    assert ps.code_text(code) != ps.code_text("int f(int x) { return x + 2; }")
