@@ -74,16 +74,20 @@ __device__ __forceinline__ u32x4 cat(const u32x2& a, const u32x2& b) {
 // row tiles first (heads of the group interleaved), in the order `reverse` asks
 // (causal forward and dQ: last tiles first, since they have the most visible keys),
 // so the heaviest tiles of the group start first and the lightest end the grid.
-__device__ __forceinline__ void map_block(int bid, int nblk, int ntile, int nhead, bool reverse,
-                                          int& head, int& tile, int hg = 1) {
-    int logical = bid;
-    if ((nblk & 7) == 0 && (nhead & 7) == 0) logical = (bid & 7) * (nblk >> 3) + (bid >> 3);
+__device__ __forceinline__ void decode_item(int logical, int ntile, int nhead, bool reverse, int& head, int& tile,
+                                            int hg = 1) {
     if (hg < 1 || ((nhead >> 3) % hg) != 0 || (nhead & 7) != 0) hg = 1;
     const int g = logical / (hg * ntile);
     const int r = logical - g * hg * ntile;
     const int t = r / hg;
     head = g * hg + (r - t * hg);
     tile = reverse ? ntile - 1 - t : t;
+}
+__device__ __forceinline__ void map_block(int bid, int nblk, int ntile, int nhead, bool reverse,
+                                          int& head, int& tile, int hg = 1) {
+    int logical = bid;
+    if ((nblk & 7) == 0 && (nhead & 7) == 0) logical = (bid & 7) * (nblk >> 3) + (bid >> 3);
+    decode_item(logical, ntile, nhead, reverse, head, tile, hg);
 }
 
 // ---------------------------------------------------------------------------------
