@@ -363,7 +363,11 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         map_block(blockIdx.x, gridDim.x, ntile_k, p.B * p.Hkv, false, head_kv, kt, 4);
         const int kt0 = kt * (C::BK / kSparseBlock);
         if (wave == 0) {
-            const int c = compact_tiles(list, nb, tid & 63, [&](int u) -> uint32_t {
+            // The layout is read down a column here (one row per lane), so batching the
+            // reads gained nothing when measured: one group at a time, each read only
+            // where the causal rule leaves the pair.
+            const int u_begin = p.causal ? min(kt0, nb) : 0;   // earlier query tiles are masked
+            const int c = compact_tiles<1>(list, u_begin, nb, tid & 63, [&](int u) -> uint32_t {
                 uint32_t bits = 0;
 #pragma unroll
                 for (int j = 0; j < C::BK / kSparseBlock; ++j) {
@@ -475,12 +479,14 @@ void fa_bwd_dq_kernel(BwdParams p) {
         const int nb = (N + kSparseBlock - 1) / kSparseBlock;
         const int qb0 = q0 / kSparseBlock;
         if (wave == 0) {
-            const int c = compact_tiles(list, nb, lane, [&](int u) -> uint32_t {
+            const int u_end = p.causal ? min(nb, qb0 + C::BR / kSparseBlock) : nb;   // later key tiles are masked
+            const int c = compact_tiles(list, 0, u_end, lane, [&](int u) -> uint32_t {
                 uint32_t bits = 0;
 #pragma unroll
                 for (int j = 0; j < C::BR / kSparseBlock; ++j) {
                     const int qb = qb0 + j;
-                    if (qb < nb && (!p.causal || u <= qb) && p.block_mask[(size_t)qb * nb + u]) bits |= 1u << j;
+                    const bool set = p.block_mask[(size_t)min(qb, nb - 1) * nb + u] != 0;
+                    bits |= (uint32_t)((qb < nb) & (!p.causal | (u <= qb)) & set) << j;
                 }
                 return bits;
             });

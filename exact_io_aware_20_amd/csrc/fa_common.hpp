@@ -279,20 +279,34 @@ constexpr int kSparseBlock = 64;
 constexpr int kSparseMaxBlocks = 2048;   // N <= 131072
 constexpr uint32_t kSparseTileMask = (1u << 20) - 1;
 
-// One wave, lanes over the candidates u in [0, n): bits(u) returns a small bit set
-// (which of the workgroup's blocks see candidate u; 0 = none).  Entries
+// One wave, lanes over the candidates u in [begin, end): bits(u) returns a small bit
+// set (which of the workgroup's blocks see candidate u; 0 = none).  Entries
 // u | bits << 20 are appended to `list` in increasing u; returns their number (the
-// same in every lane).
-template <typename F>
-__device__ __forceinline__ int compact_tiles(uint32_t* list, int n, int lane, F bits) {
+// same in every lane).  Candidates outside [begin, end) are never listed, so callers
+// narrow the range to what the causal rule leaves.  bits(u) must stay in bounds for
+// any u in the range (it is called for clamped candidates too).  BATCH groups of 64
+// candidates are evaluated before the first ballot; with a branch-free bits(u) their
+// layout reads are in flight together.
+template <int BATCH = 4, typename F>
+__device__ __forceinline__ int compact_tiles(uint32_t* list, int begin, int end, int lane, F bits) {
     int cnt = 0;
-    for (int base = 0; base < n; base += kWave) {
-        const int u = base + lane;
-        const uint32_t b = u < n ? bits(u) : 0u;
-        const uint64_t m = __ballot(b != 0u);
-        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        if (b != 0u) list[cnt + below] = (uint32_t)u | (b << 20);
-        cnt += __popcll(m);
+    for (int base = begin; base < end; base += BATCH * kWave) {
+        uint32_t b[BATCH];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+            const int u = base + i * kWave + lane;
+            const uint32_t bu = bits(min(u, end - 1));   // evaluated for every lane: no branch
+            b[i] = u < end ? bu : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+            const int u = base + i * kWave + lane;
+            const uint64_t m = __ballot(b[i] != 0u);
+            const int below =
+                __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+            if (b[i] != 0u) list[cnt + below] = (uint32_t)u | (b[i] << 20);
+            cnt += __popcll(m);
+        }
     }
     return cnt;
 }

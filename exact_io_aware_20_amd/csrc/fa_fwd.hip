@@ -588,12 +588,14 @@ void fa_fwd_sparse_kernel(FwdParams p) {
     const int nb = (N + kSparseBlock - 1) / kSparseBlock;
     const int qb0 = q0 / kSparseBlock;
     if (wave == 0) {
-        const int n = compact_tiles(list, nb, lane, [&](int u) -> uint32_t {
+        const int u_end = p.causal ? min(nb, qb0 + C::BR / kSparseBlock) : nb;   // later key tiles are masked
+        const int n = compact_tiles(list, 0, u_end, lane, [&](int u) -> uint32_t {
             uint32_t bits = 0;
 #pragma unroll
             for (int j = 0; j < C::BR / kSparseBlock; ++j) {
                 const int qb = qb0 + j;
-                if (qb < nb && (!p.causal || u <= qb) && p.block_mask[(size_t)qb * nb + u]) bits |= 1u << j;
+                const bool set = p.block_mask[(size_t)min(qb, nb - 1) * nb + u] != 0;
+                bits |= (uint32_t)((qb < nb) & (!p.causal | (u <= qb)) & set) << j;
             }
             return bits;
         });
