@@ -4,6 +4,8 @@ that bench.py reports beside its roofline.
     python -m exact_io_aware_20_amd.profile_summary trace  <trace_dir> <out.md> <warmup_launches> <command>
     python -m exact_io_aware_20_amd.profile_summary traffic <fetch_dir> <write_dir> <out.md> <calib_mib> <command>
     python -m exact_io_aware_20_amd.profile_summary mfma <pmc_dir> <out.md> <command>
+    python -m exact_io_aware_20_amd.profile_summary states <pmc_dir> <out.md> <command>
+    python -m exact_io_aware_20_amd.profile_summary lds <pmc_dir> <out.md> <command>
 
 `trace` turns a `--kernel-trace --stats` run into a table of per-kernel launch
 counts and durations.  `traffic` reads two `--pmc` runs (FETCH_SIZE, then
@@ -14,7 +16,11 @@ kernel's true bytes to what the same counter reads for it, and the per-launch HB
 bytes of every attention kernel are written with a digest of the kernel sources;
 bench.py uses the figure only while the sources still match the digest.  `mfma`
 reads a `--pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE` run and reports the share
-of SIMD cycles each attention kernel kept the matrix pipe busy.
+of SIMD cycles each attention kernel kept the matrix pipe busy.  `states` reads a
+run of the wave-state counters (STATE_COUNTERS) and splits each kernel's wave time
+into issuing, waiting at s_waitcnt or a barrier, and waiting for an issue slot or a
+dependency.  `lds` reads a run of LDS_COUNTERS and reports how busy the LDS was and
+the bytes per clock per CU it delivered to LDS loads.
 """
 from __future__ import annotations
 
@@ -226,6 +232,89 @@ def _write_mfma_md(m, out, command):
         f.write("\n".join(lines) + "\n")
 
 
+STATE_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
+                  "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_MISC")
+LDS_COUNTERS = ("SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS_LOAD_BANDWIDTH", "SQ_LDS_BANK_CONFLICT",
+                "SQ_LDS_DATA_FIFO_FULL", "GRBM_GUI_ACTIVE")
+
+
+def _kernel_counters(pmc_dir: str, counters) -> dict[str, dict[str, float]]:
+    """Per attention kernel (short name): the mean per dispatch of every counter."""
+    means = {c: counter_means(pmc_dir, c) for c in counters}
+    out = {}
+    for k in means[counters[0]]:
+        if "fa_" in k and all(k in means[c] for c in counters):
+            out[short_name(k)] = {c: means[c][k] for c in counters}
+    return out
+
+
+def wave_states(pmc_dir: str) -> dict:
+    """Shares of SQ_WAVE_CYCLES (wave-resident time summed over waves): a wave is
+    issuing (SQ_ACTIVE_INST_ANY), waiting at s_waitcnt or a barrier (SQ_WAIT_ANY), or
+    ready but not issued for a dependency or a busy pipe (SQ_WAIT_INST_ANY); the three
+    add up to about 1.  The VALU, LDS and misc rows are parts of the issuing share."""
+    out = {}
+    for k, v in _kernel_counters(pmc_dir, STATE_COUNTERS).items():
+        w = v["SQ_WAVE_CYCLES"]
+        if w > 0:
+            out[k] = {c: v[c] / w for c in STATE_COUNTERS[1:]}
+    return out
+
+
+def lds_use(pmc_dir: str) -> dict:
+    """LDS busy share SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE / XCDs x CUs) (the
+    profiler sums GRBM_GUI_ACTIVE over the XCDs; four SIMDs per CU) and the bytes per
+    clock per CU that LDS loads returned (SQ_INSTS_LDS_LOAD_BANDWIDTH counts 64-byte
+    units)."""
+    agent = gpu_agent(pmc_dir)
+    cus = agent["simds"] // 4
+    out = {}
+    for k, v in _kernel_counters(pmc_dir, LDS_COUNTERS).items():
+        cycles = v["GRBM_GUI_ACTIVE"] / agent["xcc"]
+        if cycles <= 0:
+            continue
+        out[k] = {"busy": v["SQ_LDS_IDX_ACTIVE"] / (cycles * cus),
+                  "load_bytes_per_clk_cu": 64.0 * v["SQ_INSTS_LDS_LOAD_BANDWIDTH"] / (cycles * cus),
+                  "bank_conflict": v["SQ_LDS_BANK_CONFLICT"],
+                  "fifo_full": v["SQ_LDS_DATA_FIFO_FULL"] / (cycles * cus)}
+    return {"agent": agent, "kernels": out}
+
+
+def _write_states_md(m, out, command):
+    name = os.path.splitext(os.path.basename(out))[0].replace("wave_states_", "")
+    lines = [f"# Wave states: {name}", "", "One counter run (run from the repository root; `$R` is the repository path):",
+             "", f"    {command}", "",
+             "Shares of SQ_WAVE_CYCLES (means per dispatch): `issuing` = SQ_ACTIVE_INST_ANY, `waitcnt/barrier` = "
+             "SQ_WAIT_ANY, `not issued` = SQ_WAIT_INST_ANY (ready, held by a dependency or a busy pipe); the "
+             "VALU, LDS and misc columns are parts of the issuing share, `LDS wait` of the not-issued share. "
+             f"Kernel sources digest: `{source_digest()}`.", "",
+             "| kernel | issuing | waitcnt/barrier | not issued | VALU | LDS | LDS wait | misc |",
+             "|---|---|---|---|---|---|---|---|"]
+    for k, v in sorted(m.items()):
+        lines.append(f"| {k} | {v['SQ_ACTIVE_INST_ANY']:.3f} | {v['SQ_WAIT_ANY']:.3f} | {v['SQ_WAIT_INST_ANY']:.3f} | "
+                     f"{v['SQ_ACTIVE_INST_VALU']:.3f} | {v['SQ_ACTIVE_INST_LDS']:.3f} | {v['SQ_WAIT_INST_LDS']:.3f} | "
+                     f"{v['SQ_ACTIVE_INST_MISC']:.3f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _write_lds_md(m, out, command):
+    a = m["agent"]
+    name = os.path.splitext(os.path.basename(out))[0].replace("lds_use_", "")
+    lines = [f"# LDS use: {name}", "", "One counter run (run from the repository root; `$R` is the repository path):",
+             "", f"    {command}", "",
+             f"`busy` = SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE / {a['xcc']} XCDs x {a['simds'] // 4} CUs); `B/clk/CU` = "
+             "64 x SQ_INSTS_LDS_LOAD_BANDWIDTH over the same cycles, the bytes LDS loads returned; `fifo full` = "
+             "SQ_LDS_DATA_FIFO_FULL over the same cycles (means per dispatch). "
+             f"Kernel sources digest: `{source_digest()}`.", "",
+             "| kernel | busy | B/clk/CU | bank conflict cycles | fifo full |", "|---|---|---|---|---|"]
+    for k, v in sorted(m["kernels"].items()):
+        lines.append(f"| {k} | {v['busy']:.3f} | {v['load_bytes_per_clk_cu']:.1f} | {v['bank_conflict']:.4g} | "
+                     f"{v['fifo_full']:.3f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main(argv):
     if len(argv) >= 5 and argv[0] == "trace":
         skip = int(argv[3])
@@ -234,6 +323,10 @@ def main(argv):
         _write_traffic_md(traffic(argv[1], argv[2], int(argv[4])), argv[3], argv[5])
     elif len(argv) >= 4 and argv[0] == "mfma":
         _write_mfma_md(mfma_busy(argv[1]), argv[2], argv[3])
+    elif len(argv) >= 4 and argv[0] == "states":
+        _write_states_md(wave_states(argv[1]), argv[2], argv[3])
+    elif len(argv) >= 4 and argv[0] == "lds":
+        _write_lds_md(lds_use(argv[1]), argv[2], argv[3])
     else:
         raise SystemExit(__doc__)
 

@@ -64,3 +64,39 @@ def test_digest_ignores_comments_only():
     code = "int f(int x) {\n    return x + 1;   // one more\n}\n/* block\n comment */\n"
     assert ps.code_text(code) == ps.code_text("int f(int x) { return x + 1; }")
     assert ps.code_text(code) != ps.code_text("int f(int x) { return x + 2; }")
+
+
+def _counter_dir(tmp_path, name, rows):
+    d = tmp_path / name
+    os.makedirs(d)
+    with open(d / "p_agent_info.csv", "w") as f:
+        f.write("Agent_Type,Simd_Count,Num_Xcc\nCPU,0,0\nGPU,1024,8\n")
+    with open(d / "p_counter_collection.csv", "w") as f:
+        f.write('"Kernel_Name","Counter_Name","Counter_Value"\n')
+        for k, c, v in rows:
+            f.write(f'"{k}","{c}",{v}\n')
+    return str(d)
+
+
+def test_wave_state_shares(tmp_path):
+    k = "void fa::fa_bwd_dq_kernel<128, false>(fa::BwdParams)"
+    vals = {"SQ_WAVE_CYCLES": 1000, "SQ_ACTIVE_INST_ANY": 300, "SQ_WAIT_ANY": 350, "SQ_WAIT_INST_ANY": 350,
+            "SQ_ACTIVE_INST_VALU": 200, "SQ_ACTIVE_INST_LDS": 50, "SQ_WAIT_INST_LDS": 30, "SQ_ACTIVE_INST_MISC": 10}
+    rows = [(k, c, v) for c, v in vals.items()] + [("other_kernel", "SQ_WAVE_CYCLES", 7)]
+    m = ps.wave_states(_counter_dir(tmp_path, "w", rows))
+    assert list(m) == ["fa_bwd_dq_kernel<128, false>"]
+    s = m["fa_bwd_dq_kernel<128, false>"]
+    assert abs(s["SQ_ACTIVE_INST_ANY"] + s["SQ_WAIT_ANY"] + s["SQ_WAIT_INST_ANY"] - 1.0) < 1e-12
+    assert abs(s["SQ_ACTIVE_INST_VALU"] - 0.2) < 1e-12
+
+
+def test_lds_use_per_cu(tmp_path):
+    k = "void fa::fa_fwd_bf16_kernel<128, false>(fa::FwdParams)"
+    # 8 XCDs x 1000 cycles; 256 CUs; LDS busy 250 cycles per CU; 64 B/clk per CU loaded
+    rows = [(k, "GRBM_GUI_ACTIVE", 8000), (k, "SQ_LDS_IDX_ACTIVE", 256 * 250),
+            (k, "SQ_INSTS_LDS_LOAD_BANDWIDTH", 256 * 1000), (k, "SQ_LDS_BANK_CONFLICT", 0),
+            (k, "SQ_LDS_DATA_FIFO_FULL", 0)]
+    m = ps.lds_use(_counter_dir(tmp_path, "l", rows))
+    v = m["kernels"]["fa_fwd_bf16_kernel<128, false>"]
+    assert abs(v["busy"] - 0.25) < 1e-12
+    assert abs(v["load_bytes_per_clk_cu"] - 64.0) < 1e-12
