@@ -509,6 +509,10 @@ void fa_bwd_dq_kernel(BwdParams p) {
         if (e + 1 < e_end) load_tile(tile_of(e + 1), smem + ((e + 1) & 1) * C::STAGE);
 
         if (t < wave_tiles && (!SPARSE || ((list[e] >> wbit) & 1u))) {
+            // S and dP products at raised issue priority, so that a wave in this block
+            // keeps the matrix pipe fed while its SIMD partner runs dS (measured
+            // 0.4-0.5 % faster than equal priorities)
+            __builtin_amdgcn_s_setprio(3);
             f32x16 s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
 #pragma unroll
             for (int c = 0; c < C::DC; ++c)
@@ -528,6 +532,9 @@ void fa_bwd_dq_kernel(BwdParams p) {
                         s[kb][r] = vis ? s[kb][r] : kNegInf;   // -inf * sl2 - lse2 -> p = 0
                     }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
+            __builtin_amdgcn_sched_barrier(0);
             u32x4 dsf[2][2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)

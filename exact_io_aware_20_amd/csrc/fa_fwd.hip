@@ -214,6 +214,10 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         issue_k(min(t + 2, ntiles - 1), kbuf + (t & 1) * KB);
         issue_v(t + 1, vbuf + ((t + 1) & 1) * VB);
         u32x4 pf[2][2];
+        // The wave in the mixed block below takes issue priority over its SIMD partner
+        // in the PV block, so the partner's PV MFMAs fill the gaps between this wave's
+        // exponentials (measured 0.2-0.7 % faster than equal priorities).
+        __builtin_amdgcn_s_setprio(3);
         scores_of(kbuf + ((t + 1) & 1) * KB, nxt);
         fwd_probs(cur, m_ref, sl2, pf, l_part);
         // Interleave the two in one instruction stream: four K-fragment reads ahead,
@@ -228,6 +232,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
             if (i < D / 8 - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
         pv_of(vbuf + (t & 1) * VB, pf);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
