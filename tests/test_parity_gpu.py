@@ -88,6 +88,32 @@ def test_forward_bf16_small(shape, causal):
     assert np.abs(f64(lse) - lse_ref).max() <= 1e-2
 
 
+# More 256-row blocks than compute units: the persistent forward (d = 64, and every
+# sliding window) hands each workgroup several items in turn, so the next item's
+# prefetch and the alternating K/V buffer phase run, here with ragged tails, grouped
+# heads, and head counts both divisible and not divisible by 8 (the two grid shapes).
+PERSIST = [(4, 24, 8, 1500, 64, -1), (5, 12, 4, 1100, 64, -1), (2, 32, 8, 1300, 128, 200),
+           (1, 40, 5, 2000, 128, 511)]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", PERSIST, ids=lambda s: "x".join(map(str, s)))
+def test_forward_persistent_many_items(shape, causal):
+    B, Hq, Hkv, N, d, window = shape
+    nblk = B * Hq * ((N + 255) // 256)
+    assert nblk > torch.cuda.get_device_properties(0).multi_processor_count
+    host, g = make(B, Hq, Hkv, N, d, seed=17000 + N + d)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = api.forward(g["q"], g["k"], g["v"], causal, scale, window=None if window < 0 else window)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_forward(host["q"], host["k"], host["v"], causal, scale, window=window,
+                                              workers=WORKERS)
+    err = assert_o_bf16(f64(o), o_ref, str(shape))
+    lerr = float(np.abs(f64(lse) - lse_ref).max())
+    print(f"[parity] persistent fwd {shape} blocks={nblk} causal={causal} O {err:.3e} LSE {lerr:.3e}")
+    assert lerr <= 1e-2
+
+
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("shape", [(1, 1, 1, 256, 64), (1, 1, 1, 1, 64), (2, 4, 2, 100, 128),
                                    (1, 3, 1, 33, 64), (1, 2, 2, 257, 128)],
