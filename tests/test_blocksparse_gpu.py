@@ -7,8 +7,10 @@ Bars (as for the dense bf16 path): |O - O_ref| <= 1e-2 + half a bf16 ulp,
 relative L2 <= 1e-2 for dQ, dK and dV.  Small cases use seeded random layouts (with
 empty block rows), ragged lengths, grouped-query heads, both head sizes and both
 mask settings; the local + global workload is checked at full size on sampled rows
-and two KV groups; the largest layout (2048 x 2048 blocks, N = 131072) on sampled
-forward rows and two column sums of the gradients that hold at any size.
+and two KV groups; the largest layout (2048 x 2048 blocks, N = 131072), and a ragged
+313 x 313 layout with and without the causal rule (lists built from several candidate
+groups), on sampled forward rows and two column sums of the gradients that hold at any
+size.
 """
 import math
 import sys
@@ -162,6 +164,43 @@ def test_blocksparse_largest_layout():
     nk = np.abs(f64(dk)[0, 0]).sum(axis=0)
     ev, ek = np.abs(dv_sum - do_sum), np.abs(dk_sum)
     print(f"\n[parity] blocksparse N=131072: |sum dV - sum dO| / sum|dV| {(ev / nv).max():.3e}, "
+          f"|sum dK| / sum|dK| {(ek / nk).max():.3e}")
+    assert (ev <= 1e-3 * nv).all() and (ek <= 1e-3 * nk).all()
+    assert np.isfinite(f64(dq)).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_blocksparse_multi_batch_lists(causal):
+    # N = 20000: a ragged 313 x 313 layout, so the forward and dQ build their lists from
+    # two groups of 256 candidates and dK/dV from five groups of 64; without the causal
+    # rule every candidate of a row or column is read.  Forward on sampled rows, backward
+    # through the column sums used above.
+    B, Hq, Hkv, N, d = 1, 2, 1, 20000, 64
+    host, g = make(B, Hq, Hkv, N, d, seed=16800 + causal, with_do=True)
+    lay = inputs.random_layout(N, 0.05, 16801)
+    lay[torch.arange(lay.shape[0]), torch.arange(lay.shape[0])] = 1     # every row sees its own block
+    scale = 1.0 / math.sqrt(d)
+    o, lse = api.forward(g["q"], g["k"], g["v"], causal, scale, block_mask=lay.to(dev()))
+    dq, dk, dv = api.backward(g["q"], g["k"], g["v"], o, g["do"], lse, causal, scale, block_mask=lay.to(dev()))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(16802)
+    # one random row of every 64-row block (so every block row's list is exercised),
+    # plus the first and the ragged last rows
+    per_block = np.minimum(np.arange(0, N, 64) + rng.integers(0, 64, size=(N + 63) // 64), N - 1)
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(N - 96, N), per_block]))
+    o_ref, lse_ref = oracle.attention_forward(host["q"], host["k"], host["v"], causal, scale, rows=rows,
+                                              block_mask=lay.numpy().astype(bool), workers=WORKERS)
+    for h in range(Hq):
+        assert_o_bf16(f64(o)[0, h, rows], o_ref[0, h, rows], f"multi-batch head {h}")
+        assert np.abs(f64(lse)[0, h, rows] - lse_ref[0, h, rows]).max() <= 1e-2
+    # one KV head serves both query heads: its dV column sums equal the dO sums of both
+    do_sum = host["do"].double().sum(dim=(1, 2))[0].numpy()
+    dv_sum = dv.double().sum(dim=2)[0, 0].cpu().numpy()
+    dk_sum = dk.double().sum(dim=2)[0, 0].cpu().numpy()
+    nv = np.abs(f64(dv)[0, 0]).sum(axis=0)
+    nk = np.abs(f64(dk)[0, 0]).sum(axis=0)
+    ev, ek = np.abs(dv_sum - do_sum), np.abs(dk_sum)
+    print(f"\n[parity] blocksparse N=20000 causal={causal}: |sum dV - sum dO| / sum|dV| {(ev / nv).max():.3e}, "
           f"|sum dK| / sum|dK| {(ek / nk).max():.3e}")
     assert (ev <= 1e-3 * nv).all() and (ek <= 1e-3 * nk).all()
     assert np.isfinite(f64(dq)).all()
