@@ -13,7 +13,8 @@ import pytest
 import torch
 
 from oracle import (attention_backward, attention_forward, head_backward, head_forward,
-                    head_forward_tiled, head_probs, online_softmax_states)
+                    head_forward_merged, head_probs, merge_states, online_softmax_states,
+                    tile_state)
 
 GOLDEN = Path(__file__).parent / "golden"
 
@@ -163,13 +164,15 @@ def test_rows_subset_matches_full():
 
 # ------------------------------------------------------------------ P5: online == two-pass
 
-@pytest.mark.parametrize("br,bc", [(1, 1), (3, 5), (16, 7), (128, 128), (64, 32)])
+@pytest.mark.parametrize("bc", [1, 5, 7, 32, 128, 200])
+@pytest.mark.parametrize("seed", [0, 1])
 @pytest.mark.parametrize("causal", [True, False])
-def test_online_tiled_equals_two_pass(br, bc, causal):
+def test_online_merged_equals_two_pass(bc, seed, causal):
+    # tiles' partial states merged in a seeded tree order reach the two-pass result
     n, d = 133, 16
     q, k, v = rand((n, d), 20, 3.0), rand((n, d), 21, 3.0), rand((n, d), 22)
     o1, l1 = head_forward(q, k, v, causal, 0.25)
-    o2, l2 = head_forward_tiled(q, k, v, causal, 0.25, br, bc)
+    o2, l2 = head_forward_merged(q, k, v, causal, 0.25, bc, seed)
     assert np.abs(o1 - o2).max() <= 1e-12 * max(1.0, np.abs(o1).max())
     assert np.abs(l1 - l2).max() <= 1e-12 * max(1.0, np.abs(l1).max())
 
@@ -179,9 +182,37 @@ def test_online_large_logits():
     n, d = 96, 16
     q, k, v = rand((n, d), 23, 8.0), rand((n, d), 24, 8.0), rand((n, d), 25)
     o1, l1 = head_forward(q, k, v, True, 0.25)
-    o2, l2 = head_forward_tiled(q, k, v, True, 0.25, 16, 32)
+    o2, l2 = head_forward_merged(q, k, v, True, 0.25, 32, 3)
     assert np.isfinite(o1).all() and np.abs(l1).max() > 50
     assert np.abs(o1 - o2).max() < 1e-12 and np.abs(l1 - l2).max() < 1e-9
+
+
+def test_merge_is_the_state_of_the_union_by_hand():
+    # one row, scores (0, ln 2 | ln 3) with values (1, 2 | 3): A = {0, ln 2} has
+    # m = ln 2, l = 1/2 + 1 = 3/2, a = 1/2 + 2 = 5/2; B = {ln 3} has m = ln 3, l = 1,
+    # a = 3; the union has m = ln 3, l = (3/2)(2/3) + 1 = 2, a = (5/2)(2/3) + 3 = 14/3
+    # (the three-element example's last state), and output 7/3.
+    sa = np.array([[0.0, math.log(2.0)]])
+    sb = np.array([[math.log(3.0)]])
+    A = tile_state(sa, np.array([[1.0], [2.0]]))
+    B = tile_state(sb, np.array([[3.0]]))
+    assert A[0][0] == pytest.approx(math.log(2.0), abs=1e-15)
+    assert A[1][0] == pytest.approx(1.5, rel=1e-15) and A[2][0, 0] == pytest.approx(2.5, rel=1e-15)
+    for m, l, a in (merge_states(A, B), merge_states(B, A)):
+        assert m[0] == pytest.approx(math.log(3.0), abs=1e-15)
+        assert l[0] == pytest.approx(2.0, rel=1e-15)
+        assert a[0, 0] == pytest.approx(14 / 3, rel=1e-15)
+        assert a[0, 0] / l[0] == pytest.approx(7 / 3, rel=1e-15)
+
+
+def test_merge_identity_and_hidden_tile():
+    # a tile whose keys are all hidden from a row is the merge's identity for that row
+    s = np.array([[-np.inf, -np.inf], [0.5, -np.inf]])
+    m, l, a = tile_state(s, np.array([[1.0], [2.0]]))
+    assert m[0] == -np.inf and l[0] == 0.0 and a[0, 0] == 0.0
+    other = (np.array([0.25, 0.25]), np.array([2.0, 2.0]), np.array([[3.0], [3.0]]))
+    m2, l2, a2 = merge_states((m, l, a), other)
+    assert m2[0] == 0.25 and l2[0] == 2.0 and a2[0, 0] == 3.0
 
 
 # ------------------------------------------------------------------ P7: grouped-query heads
