@@ -15,7 +15,7 @@ CSRC = PKG / "csrc"
 ROOT = PKG.parent
 LIB = PKG / "libfa_mi355x.so"
 OBJ_DIR = ROOT / "_build"
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_decode.hip", "fa_plan.cpp", "fa_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 VALU forms are kept out of every kernel; hipcc's host pass warns that

@@ -14,7 +14,7 @@ constexpr long long kMaxGrid = 0x7fffffffLL;
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Two fp32 per query row: D (dO . O) and LSE in base-2 units.
-size_t workspace_bytes(int B, int Hq, int N) {
+size_t bwd_ws_bytes(int B, int Hq, int N) {
     if (B < 1 || Hq < 1 || N < 1) return 0;
     return (size_t)B * Hq * N * 2 * sizeof(float);
 }
@@ -76,7 +76,7 @@ fa_status check_bwd(BwdStep step, const void* q, const void* k, const void* v, c
     fa_status s = check_shape(B, Hq, Hkv, N, d, causal, scale);
     if (s != FA_OK) return s;
     if (fa::bwd_grid_max(B, Hq, Hkv, N, d) > kMaxGrid) return FA_ERR_SHAPE;
-    const size_t ws_need = workspace_bytes(B, Hq, N);
+    const size_t ws_need = bwd_ws_bytes(B, Hq, N);
     if (!workspace || !aligned16(workspace) || ws_bytes < ws_need) return FA_ERR_WORKSPACE;
     const uintptr_t qb = (uintptr_t)B * Hq * N * d * 2, kb = (uintptr_t)B * Hkv * N * d * 2;
     const uintptr_t lb = (uintptr_t)B * Hq * N * 4;
@@ -354,7 +354,7 @@ fa_status fa_decode_paged_forward(FA_PAGED_ARGS) {
 fa_status fa_decode_paged_split(FA_PAGED_ARGS) { return paged_call(fa::kDecodeSplit, FA_PAGED_PASS); }
 fa_status fa_decode_paged_merge(FA_PAGED_ARGS) { return paged_call(fa::kDecodeMerge, FA_PAGED_PASS); }
 
-size_t fa_backward_workspace_bytes(int B, int Hq, int N) { return workspace_bytes(B, Hq, N); }
+size_t fa_backward_workspace_bytes(int B, int Hq, int N) { return bwd_ws_bytes(B, Hq, N); }
 
 fa_status fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO,
                       const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
@@ -458,7 +458,9 @@ static fa_status bwd_blocksparse(int steps, const void* q, const void* k, const 
     const uintptr_t qb = (uintptr_t)B * Hq * N * d * 2, kb = (uintptr_t)B * Hkv * N * d * 2;
     const void* outs[4] = {(steps & 4) ? dq : nullptr, (steps & 2) ? dk : nullptr, (steps & 2) ? dv : nullptr,
                            (steps & 1) ? workspace : nullptr};
-    const uintptr_t ob[4] = {qb, kb, kb, workspace_bytes};
+    // the workspace's extent is what the call uses (the caller's figure may be any
+    // larger value, and adding it to the address could wrap)
+    const uintptr_t ob[4] = {qb, kb, kb, (uintptr_t)bwd_ws_bytes(B, Hq, N)};
     if ((s = check_layout(block_mask, outs, ob, 4, N)) != FA_OK) return s;
     fa::BwdParams p = bwd_params(q, k, v, o, dO, lse, dq, dk, dv, workspace, B, Hq, Hkv, N, causal, scale);
     p.block_mask = block_mask;

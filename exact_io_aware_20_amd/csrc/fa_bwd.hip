@@ -83,6 +83,7 @@ struct DkdvCfg {
     static constexpr int STAGE = 2 * NAT + 2 * BQ * 2;  // Q, dO, then LSE2 and D (fp32, BQ each)
     static constexpr int NSTAGE = 3;                    // items it+1 (loading), it, it-1
     static constexpr int PBUF = 2 * 4 * 32 * 64;        // bf16 P of two items: 2 x 4 pairs x 32 keys x 64 queries
+    static_assert(BK == kDkdvKeys, "launch plan and kernel disagree on the key tile");
 };
 
 // Element offsets of the row fragments (row l32, chunk 2k + hh) of a MODE 1 tile;
@@ -401,6 +402,7 @@ struct DqCfg {
     static constexpr int KT = SwzTile<D, 1>::ELEMS;   // K: fragment and transposing reads
     static constexpr int VT = SwzTile<D, 0>::ELEMS;   // V: fragment reads
     static constexpr int STAGE = KT + VT;
+    static_assert(BR == kDqRows, "launch plan and kernel disagree on the row tile");
 };
 
 // dQ kernel: per key/value tile, S^T = K Q^T and dP^T = V dO^T (lane: query),
@@ -574,14 +576,6 @@ void fa_bwd_dq_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------
-long long bwd_grid_max(int B, int Hq, int Hkv, int N, int d) {
-    const long long pre = ((long long)B * Hq * N * (d / 8) + kThreads - 1) / kThreads;
-    const long long dkdv = (long long)B * Hkv * ((N + 127) / 128);
-    const long long dq = (long long)B * Hq * ((N + 255) / 256);
-    long long m = pre > dkdv ? pre : dkdv;
-    return m > dq ? m : dq;
-}
-
 template <int D>
 static hipError_t launch_pre(const BwdParams& p, hipStream_t stream) {
     const long long rows = (long long)p.B * p.Hq * p.N;

@@ -34,13 +34,6 @@
 
 namespace fa {
 
-constexpr int kDecodeTile = 64;           // keys per K/V tile
-// One single-wave workgroup per SIMD: four per CU on 256 CUs.  Paged calls plan for
-// their longest sequence (the only length the host knows), so with mixed lengths the
-// splits past a shorter sequence's end exit at once; planning more, shorter splits
-// (2048 to 4096), or issuing splits before sequences, measured slower.
-constexpr int kDecodeTargetWgs = 1024;
-
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8); the counters not named are left at their maximum.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -301,22 +294,6 @@ __global__ __launch_bounds__(256) void fa_decode_merge_kernel(DecodeParams p) {
 // ---------------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------------
-DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
-    DecodePlan pl{};
-    const long long target = kDecodeTargetWgs;
-    const long long G = Hq / Hkv;
-    const long long ntiles = (Nk + kDecodeTile - 1) / kDecodeTile;
-    pl.nrb = (int)((G * Nq + 31) / 32);
-    const long long units = (long long)B * Hkv * pl.nrb;   // workgroups per split
-    long long per = (ntiles * units + target - 1) / target;
-    per = per < 1 ? 1 : (per > ntiles ? ntiles : per);
-    pl.tiles_per_split = (int)per;
-    pl.nsplit = (int)((ntiles + per - 1) / per);
-    pl.grid = units * pl.nsplit;
-    pl.workspace_bytes = (size_t)pl.nsplit * B * Hq * Nq * (size_t)(d + 1) * sizeof(float);
-    return pl;
-}
-
 template <int D>
 static hipError_t launch_decode_d(const DecodeParams& p, int steps, bool paged, hipStream_t stream) {
     if (steps & kDecodeSplit) {

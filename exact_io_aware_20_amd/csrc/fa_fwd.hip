@@ -43,6 +43,7 @@ struct FwdCfg {
     static constexpr int BC = 64;                 // keys per K/V tile
     static constexpr int DC = D / 16;             // k-chunks of the S contraction
     static constexpr int DB = D / 32;             // 32-row blocks of O^T
+    static_assert(BR == kFwdRows, "launch plan and kernel disagree on the row tile");
 };
 
 // Loop-hoisted LDS addressing of the K fragments: the swizzle depends on the row mod
@@ -786,11 +787,13 @@ static hipError_t launch_bf16(const FwdParams& p, hipStream_t stream) {
         hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, false>), dim3((unsigned)nblk), dim3(FwdCfg<D>::THREADS), 0, stream,
                            p);
     } else {
-        // sliding window (4 % faster persistent) and d = 64 (2 % faster)
+        // sliding window (4 % faster persistent) and d = 64 (2 % faster): one workgroup
+        // per compute unit of the device the stream belongs to
         int dev = 0, ncu = 0;
-        hipError_t e = hipGetDevice(&dev);
+        hipError_t e = hipStreamGetDevice(stream, &dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
+        if (ncu < 1) return hipErrorInvalidDevice;
         const long long nhead = (long long)p.B * p.Hq;
         long long grid = nblk < ncu ? nblk : ncu;
         if ((nblk & 7) == 0 && (nhead & 7) == 0 && grid >= 8) grid -= grid & 7;
@@ -804,16 +807,9 @@ static hipError_t launch_bf16(const FwdParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-long long fwd_bf16_grid(int B, int Hq, int N, int d) {
-    const int br = d == 64 ? FwdCfg<64>::BR : FwdCfg<128>::BR;
-    return (long long)B * Hq * ((N + br - 1) / br);
-}
-
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t stream) {
     return d == 64 ? launch_bf16<64>(p, stream) : launch_bf16<128>(p, stream);
 }
-
-long long fwd_f32_grid(int B, int Hq, int N) { return (long long)B * Hq * ((N + 31) / 32); }
 
 hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t stream) {
     const unsigned nblk = (unsigned)fwd_f32_grid(p.B, p.Hq, p.N);

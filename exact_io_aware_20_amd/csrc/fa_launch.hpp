@@ -10,6 +10,18 @@ namespace fa {
 constexpr int kSparseBlockHost = 64;
 constexpr int kSparseMaxBlocksHost = 2048;
 
+// Workgroup tiles the launch plans are made of (the kernels assert they match).
+constexpr int kFwdRows = 256;     // query rows per forward workgroup (8 waves x 32)
+constexpr int kFwdF32Rows = 32;   // query rows per fp32 forward workgroup
+constexpr int kDkdvKeys = 128;    // keys per dK/dV workgroup
+constexpr int kDqRows = 256;      // query rows per dQ workgroup
+constexpr int kDecodeTile = 64;   // keys per decode K/V tile
+// Decode: one single-wave workgroup per SIMD, four per CU on 256 CUs.  Paged calls plan
+// for their longest sequence (the only length the host knows), so with mixed lengths the
+// splits past a shorter sequence's end exit at once; planning more, shorter splits
+// (2048 to 4096), or issuing splits before sequences, measured slower.
+constexpr int kDecodeTargetWgs = 1024;
+
 struct FwdParams {
     const void* q;
     const void* k;

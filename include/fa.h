@@ -65,9 +65,17 @@ typedef enum fa_status {
 
 /*
  * Forward pass, bf16 inputs and outputs, fp32 accumulation and softmax state.
+ * Defined by: "LLM interview question bank" ch.029 #36, sections 2-3 (Q, K, V in
+ * R^(B x H x L x d); query tiles walk the K/V tiles with a running max and
+ * denominator, the score tile stays on chip, O is written once); lecture summary,
+ * "GPU 显存和注意力瓶颈" (the causal rule, diagonal included) and "减少缓存表示并验证草稿"
+ * (Hq query heads over Hkv key/value heads); "推导 FlashAttention 的在线 softmax" (the
+ * small per-row statistic kept for the backward pass: here the natural-log LSE).
  * q [B,Hq,N,d], k and v [B,Hkv,N,d] (bf16, read only); o [B,Hq,N,d] bf16 and
  * lse [B,Hq,N] fp32 are overwritten.  P is rounded to bf16 (round to nearest
  * even) before the P.V contraction, and O is rounded to bf16 on store.
+ * Errors: FA_ERR_NULL, _SHAPE, _GQA, _HEADDIM, _FLAG, _SCALE, _ALIGN, _ALIAS
+ * (nothing launched), FA_ERR_LAUNCH.
  */
 fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int Hq, int Hkv, int N, int d, int causal, float scale,
@@ -75,20 +83,28 @@ fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float
 
 /*
  * Forward pass with every tensor and every intermediate in fp32 (no reduced
- * precision anywhere).  Same shapes, layout and rules as fa_forward.
+ * precision anywhere).  Same definition and sources as fa_forward (the pages fix no
+ * precision; this is the path held to 1e-5 of the exact result).  Same shapes, layout,
+ * rules and errors as fa_forward, with 4-byte elements.
  */
 fa_status fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                          int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                          hipStream_t stream);
 
 /* Bytes of device workspace fa_backward needs: two fp32 per query row (the
- * per-row term D_i = sum_t dO_it * O_it, and LSE_i in base-2 units).  Returns 0
- * for invalid sizes. */
+ * per-row term D_i = sum_t dO_it * O_it, and LSE_i in base-2 units; lecture summary,
+ * "推导 FlashAttention 的在线 softmax": the backward pass rebuilds P from the small
+ * saved statistic).  Returns 0 for invalid sizes (B, Hq or N < 1). */
 size_t fa_backward_workspace_bytes(int B, int Hq, int N);
 
 /*
  * Backward pass for L with upstream gradient dO = dL/dO, bf16, recomputing P
- * tile by tile from the saved lse (the small statistic the forward keeps):
+ * tile by tile from the saved lse (the small statistic the forward keeps).
+ * Defined by: code-corey Q38, section 2.(2) 重计算 (S and P are not stored, they are
+ * recomputed in the backward pass); lecture summary, "推导 FlashAttention 的在线
+ * softmax" (the backward pass works from the saved statistic); "LLM interview question
+ * bank" ch.029 #36, section 7 (the backward costs 2.2-2.5x the forward).  The
+ * gradients are the softmax-Jacobian ones (the pages print none):
  *   dP = dO V^T,  D_i = sum_j P_ij dP_ij = dO_i . O_i,  dS = P * (dP - D),
  *   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
  * q, k, v, o, dO (bf16) and lse (fp32) are the forward's inputs and outputs.
@@ -96,6 +112,8 @@ size_t fa_backward_workspace_bytes(int B, int Hq, int N);
  * dk and dv of a KV head are the sums over the Hq/Hkv query heads of its group.
  * workspace: device memory of at least fa_backward_workspace_bytes(B,Hq,N)
  * bytes (passed in workspace_bytes), 16-byte aligned, clobbered by the call.
+ * Errors: those of fa_forward, and FA_ERR_WORKSPACE (NULL, misaligned or smaller
+ * than required); the workspace may overlap no tensor argument (FA_ERR_ALIAS).
  */
 fa_status fa_backward(const void* q, const void* k, const void* v, const void* o,
                       const void* dO, const float* lse, void* dq, void* dk, void* dv,
@@ -104,7 +122,9 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
                       hipStream_t stream);
 
 /*
- * The three steps fa_backward enqueues, in this order, exposed so that a caller
+ * The three steps fa_backward enqueues, in this order (same sources as fa_backward:
+ * the preprocess forms the per-row term of the softmax Jacobian, D_i = dO_i . O_i;
+ * the other two recompute P from the saved statistic), exposed so that a caller
  * can place them itself (after fa_backward_preprocess, fa_backward_dkdv and
  * fa_backward_dq only read the workspace and may run concurrently on two
  * streams).  Arguments, layouts and errors are those of fa_backward.

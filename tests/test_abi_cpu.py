@@ -1,7 +1,16 @@
 """The C-ABI library loads, exports what include/fa.h declares, and validates
-arguments on the host (no GPU needed: nothing here launches a kernel)."""
+arguments on the host (no GPU needed: nothing here launches a kernel).
+
+If the library has not been built, it is built here first (hipcc cross-compiles the
+gfx950 code without a GPU), so these checks always run.  The same module also runs
+against a host-only build of the ABI (fa_api.cpp and the launch plans, with counting
+stand-ins for the launchers) made with AddressSanitizer and UndefinedBehaviorSanitizer
+by tests/test_abi_host_asan.py; the tests marked ``stub_only`` need that build, since
+they make calls that pass validation and would launch kernels in the real library.
+"""
 import ctypes
 import math
+import os
 import re
 from pathlib import Path
 
@@ -12,8 +21,28 @@ from exact_io_aware_20_amd import api
 ROOT = Path(__file__).resolve().parents[1]
 HEADER = ROOT / "include" / "fa.h"
 
-pytestmark = pytest.mark.skipif(not api.LIB_PATH.exists(),
-                                reason="libfa_mi355x.so not built (python -m exact_io_aware_20_amd.build)")
+
+@pytest.fixture(scope="module", autouse=True)
+def _library():
+    if not api.LIB_PATH.exists() and "FA_MI355X_LIB" not in os.environ:
+        from exact_io_aware_20_amd.build import build_library
+        build_library()
+    assert api.LIB_PATH.exists(), api.LIB_PATH
+    yield
+
+
+def _is_stub() -> bool:
+    return hasattr(api.load_library(), "fa_stub_launches")
+
+
+def stub_only(fn):
+    """Run only against the host-only sanitizer build (the calls pass validation)."""
+    def wrapper(*a, **kw):
+        if not _is_stub():
+            pytest.skip("needs the host-only ABI build (tests/test_abi_host_asan.py runs it)")
+        return fn(*a, **kw)
+    wrapper.__name__ = fn.__name__
+    return wrapper
 
 
 def declared_functions():
@@ -27,6 +56,7 @@ def test_header_declares_the_binding_entry_points():
 
 def test_library_exports_every_declared_symbol():
     lib = ctypes.CDLL(str(api.LIB_PATH))
+    assert not _is_stub() or os.environ.get("FA_MI355X_LIB")
     for name in declared_functions():
         assert hasattr(lib, name), name
 
@@ -221,3 +251,118 @@ def test_blocksparse_calls_reject_before_launch():
     assert lib.fa_backward_dkdv_blocksparse(Q, K, V, dO, ws, need - 4, dk, dv, BM, 1, 2, 1, 16, 64, 1, 0.1,
                                             None) == 8
     assert lib.fa_backward_dq_blocksparse(Q, K, V, dO, ws, need, dq, BM, 1, 3, 2, 16, 64, 1, 0.1, None) == 3
+
+
+def test_blocksparse_layout_inside_workspace_is_an_alias_whatever_workspace_bytes_says():
+    # The overlap test uses the workspace extent the call writes, not the caller's
+    # figure: with SIZE_MAX the end address would wrap and hide the overlap.
+    lib = api.load_library()
+    dO, ws, dq, dk, dv = 0x20_0000_0000, 0x60_0000_0000, 0x30_0000_0000, 0x40_0000_0000, 0x50_0000_0000
+    need = lib.fa_backward_workspace_bytes(1, 2, 16)
+    huge = (1 << 64) - 1
+    inside = ws + 64
+    assert lib.fa_backward_blocksparse(Q, K, V, O, dO, L, dq, dk, dv, inside, ws, huge, 1, 2, 1, 16, 64, 1, 0.1,
+                                       None) == 9
+    assert lib.fa_backward_blocksparse(Q, K, V, O, dO, L, dq, dk, dv, inside, ws, need, 1, 2, 1, 16, 64, 1, 0.1,
+                                       None) == 9
+
+
+# ---------------------------------------------------------------- host-only build: calls that pass
+
+def _launches():
+    return api.load_library().fa_stub_launches()
+
+
+@stub_only
+def test_every_entry_point_launches_only_after_validation():
+    lib = api.load_library()
+    lib.fa_stub_launches.restype = ctypes.c_longlong
+    dO, ws, dq, dk, dv, BM = (0x20_0000_0000, 0x60_0000_0000, 0x30_0000_0000, 0x40_0000_0000, 0x50_0000_0000,
+                              0x80_0000_0000)
+    KP, VP, TB, SL = 0x70_0000_0000, 0x71_0000_0000, 0x72_0000_0000, 0x73_0000_0000
+    need = lib.fa_backward_workspace_bytes(2, 4, 300)
+    dneed = lib.fa_decode_workspace_bytes(2, 4, 2, 3, 1000, 128)
+    # (name, launcher calls when valid (decode: one call covers its split and merge),
+    #  valid call, a rejected variant)
+    calls = [
+        ("fa_forward", 1, lambda c: lib.fa_forward(Q, K, V, O, L, 2, 4, 2, 300, 128, c, 0.1, None),
+         lambda: lib.fa_forward(Q, K, V, O, L, 2, 4, 2, 300, 96, 1, 0.1, None)),
+        ("fa_forward_f32", 1, lambda c: lib.fa_forward_f32(Q, K, V, O, L, 2, 4, 2, 300, 64, c, 0.1, None),
+         lambda: lib.fa_forward_f32(Q, K, V, Q, L, 2, 4, 2, 300, 64, 1, 0.1, None)),
+        ("fa_backward", 3, lambda c: lib.fa_backward(Q, K, V, O, dO, L, dq, dk, dv, ws, need, 2, 4, 2, 300, 128, c,
+                                                      0.1, None),
+         lambda: lib.fa_backward(Q, K, V, O, dO, L, dq, dk, dv, ws, need - 1, 2, 4, 2, 300, 128, 1, 0.1, None)),
+        ("fa_backward_preprocess", 1, lambda c: lib.fa_backward_preprocess(O, dO, L, ws, need, 2, 4, 300, 128, None),
+         lambda: lib.fa_backward_preprocess(O, dO, L, O, need, 2, 4, 300, 128, None)),
+        ("fa_backward_dkdv", 1, lambda c: lib.fa_backward_dkdv(Q, K, V, dO, ws, need, dk, dv, 2, 4, 2, 300, 64, c,
+                                                                0.1, None),
+         lambda: lib.fa_backward_dkdv(Q, K, V, dO, ws, need, dk, K, 2, 4, 2, 300, 64, 1, 0.1, None)),
+        ("fa_backward_dq", 1, lambda c: lib.fa_backward_dq(Q, K, V, dO, ws, need, dq, 2, 4, 2, 300, 64, c, 0.1,
+                                                            None),
+         lambda: lib.fa_backward_dq(Q, K, V, dO, ws, need, dq, 2, 4, 3, 300, 64, 1, 0.1, None)),
+        ("fa_forward_window", 1, lambda c: lib.fa_forward_window(Q, K, V, O, L, 2, 4, 2, 300, 128, c, 17, 0.1,
+                                                                  None),
+         lambda: lib.fa_forward_window(Q, K, V, O, L, 2, 4, 2, 300, 128, 1, -2, 0.1, None)),
+        ("fa_backward_window", 3, lambda c: lib.fa_backward_window(Q, K, V, O, dO, L, dq, dk, dv, ws, need, 2, 4, 2,
+                                                                    300, 128, c, 17, 0.1, None),
+         lambda: lib.fa_backward_window(Q, K, V, O, dO, L, dq, dk, dv, ws, need, 2, 4, 2, 300, 128, 1, 17,
+                                        float("inf"), None)),
+        ("fa_backward_dkdv_window", 1, lambda c: lib.fa_backward_dkdv_window(Q, K, V, dO, ws, need, dk, dv, 2, 4, 2,
+                                                                              300, 64, c, 5, 0.1, None),
+         lambda: lib.fa_backward_dkdv_window(Q, K, V, dO, ws, need, dk, dv, 2, 4, 2, 300, 64, 1, -1, 0.1, None)),
+        ("fa_backward_dq_window", 1, lambda c: lib.fa_backward_dq_window(Q, K, V, dO, ws, need, dq, 2, 4, 2, 300,
+                                                                          64, c, 5, 0.1, None),
+         lambda: lib.fa_backward_dq_window(Q, K, V, dO, None, need, dq, 2, 4, 2, 300, 64, 1, 5, 0.1, None)),
+        ("fa_forward_blocksparse", 1, lambda c: lib.fa_forward_blocksparse(Q, K, V, O, L, BM, 2, 4, 2, 300, 128, c,
+                                                                            0.1, None),
+         lambda: lib.fa_forward_blocksparse(Q, K, V, O, L, L, 2, 4, 2, 300, 128, 1, 0.1, None)),
+        ("fa_backward_blocksparse", 3, lambda c: lib.fa_backward_blocksparse(Q, K, V, O, dO, L, dq, dk, dv, BM, ws,
+                                                                              need, 2, 4, 2, 300, 128, c, 0.1, None),
+         lambda: lib.fa_backward_blocksparse(Q, K, V, O, dO, L, dq, dk, dv, dk, ws, need, 2, 4, 2, 300, 128, 1,
+                                             0.1, None)),
+        ("fa_backward_dkdv_blocksparse", 1,
+         lambda c: lib.fa_backward_dkdv_blocksparse(Q, K, V, dO, ws, need, dk, dv, BM, 2, 4, 2, 300, 64, c, 0.1,
+                                                    None),
+         lambda: lib.fa_backward_dkdv_blocksparse(Q, K, V, dO, ws, need, dk, dv, None, 2, 4, 2, 300, 64, 1, 0.1,
+                                                  None)),
+        ("fa_backward_dq_blocksparse", 1,
+         lambda c: lib.fa_backward_dq_blocksparse(Q, K, V, dO, ws, need, dq, BM, 2, 4, 2, 300, 64, c, 0.1, None),
+         lambda: lib.fa_backward_dq_blocksparse(Q, K, V, dO, ws, need, dq, BM, 2, 4, 2, 300, 64, 5, 0.1, None)),
+        ("fa_decode_forward", 1, lambda c: lib.fa_decode_forward(Q, K, V, O, L, ws, dneed, 2, 4, 2, 3, 1000, 128, c,
+                                                                  0.1, None),
+         lambda: lib.fa_decode_forward(Q, K, V, O, L, ws, dneed - 1, 2, 4, 2, 3, 1000, 128, 1, 0.1, None)),
+        ("fa_decode_split", 1, lambda c: lib.fa_decode_split(Q, K, V, O, L, ws, dneed, 2, 4, 2, 3, 1000, 128, c,
+                                                              0.1, None),
+         lambda: lib.fa_decode_split(Q, K, V, O, L, ws, dneed, 2, 4, 2, 1001, 1000, 128, 1, 0.1, None)),
+        ("fa_decode_merge", 1, lambda c: lib.fa_decode_merge(Q, K, V, O, L, ws, dneed, 2, 4, 2, 3, 1000, 128, c,
+                                                              0.1, None),
+         lambda: lib.fa_decode_merge(Q, K, V, O, L, K, dneed, 2, 4, 2, 3, 1000, 128, 1, 0.1, None)),
+        ("fa_decode_paged_forward", 1,
+         lambda c: lib.fa_decode_paged_forward(Q, KP, VP, TB, SL, O, L, ws, dneed, 2, 4, 2, 3, 1000, 10, 128, 8,
+                                               128, c, 0.1, None),
+         lambda: lib.fa_decode_paged_forward(Q, KP, VP, TB, SL, O, L, ws, dneed, 2, 4, 2, 3, 1000, 10, 100, 8,
+                                             128, 1, 0.1, None)),
+        ("fa_decode_paged_split", 1,
+         lambda c: lib.fa_decode_paged_split(Q, KP, VP, TB, SL, O, L, ws, dneed, 2, 4, 2, 3, 1000, 10, 128, 8,
+                                             128, c, 0.1, None),
+         lambda: lib.fa_decode_paged_split(Q, KP, VP, TB + 1, SL, O, L, ws, dneed, 2, 4, 2, 3, 1000, 10, 128, 8,
+                                           128, 1, 0.1, None)),
+        ("fa_decode_paged_merge", 1,
+         lambda c: lib.fa_decode_paged_merge(Q, KP, VP, TB, SL, O, L, ws, dneed, 2, 4, 2, 3, 1000, 10, 128, 8,
+                                             128, c, 0.1, None),
+         lambda: lib.fa_decode_paged_merge(Q, KP, VP, TB, SL, O, L, ws, dneed, 2, 4, 2, 3, 1000, 10, 128, 7,
+                                           128, 1, 0.1, None)),
+    ]
+    named = {c[0] for c in calls}
+    computing = {n for n in declared_functions()
+                 if n not in ("fa_backward_workspace_bytes", "fa_decode_workspace_bytes", "fa_check_args",
+                              "fa_status_string")}
+    assert computing <= named, sorted(computing - named)
+    for name, n_launch, ok, bad in calls:
+        for causal in (0, 1):
+            before = _launches()
+            assert ok(causal) == 0, name
+            assert _launches() - before == n_launch, name
+        before = _launches()
+        assert bad() != 0, name
+        assert _launches() == before, name
