@@ -19,7 +19,7 @@ FA_STATUS = {
     5: "FA_ERR_SCALE", 6: "FA_ERR_ALIGN", 7: "FA_ERR_FLAG", 8: "FA_ERR_WORKSPACE",
     9: "FA_ERR_ALIAS", 10: "FA_ERR_LAUNCH", 11: "FA_ERR_WINDOW",
 }
-ENTRY_POINTS = ("fa_forward", "fa_forward_f32", "fa_backward", "fa_backward_workspace_bytes",
+ENTRY_POINTS = ("fa_forward", "fa_forward_f32", "fa_forward_fp32_out", "fa_backward", "fa_backward_workspace_bytes",
                 "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq",
                 "fa_decode_forward", "fa_decode_workspace_bytes", "fa_decode_split", "fa_decode_merge",
                 "fa_forward_window", "fa_backward_window", "fa_backward_dkdv_window", "fa_backward_dq_window",
@@ -50,6 +50,8 @@ def load_library() -> ctypes.CDLL:
     lib.fa_forward.restype = i
     lib.fa_forward_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     lib.fa_forward_f32.restype = i
+    lib.fa_forward_fp32_out.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_forward_fp32_out.restype = i
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
     lib.fa_backward.restype = i
     lib.fa_backward_preprocess.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, vp]
@@ -132,6 +134,24 @@ def forward(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None, 
     if window is not None:
         return _forward("fa_forward_window", torch.bfloat16, q, k, v, causal, scale, o, lse, stream, window)
     return _forward("fa_forward", torch.bfloat16, q, k, v, causal, scale, o, lse, stream)
+
+
+def forward_fp32_out(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None):
+    """Validation diagnostic via fa_forward_fp32_out: bf16 q, k, v; O returned in fp32
+    as the bf16 kernel computes it before its final rounding.  Returns (o, lse)."""
+    lib = load_library()
+    B, Hq, Hkv, N, d = _shape(q, k)
+    _require(q, "q", torch.bfloat16, (B, Hq, N, d))
+    _require(k, "k", torch.bfloat16, (B, Hkv, N, d))
+    _require(v, "v", torch.bfloat16, (B, Hkv, N, d))
+    o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device) if o is None else o
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _require(o, "o", torch.float32, (B, Hq, N, d))
+    _require(lse, "lse", torch.float32, (B, Hq, N))
+    code = lib.fa_forward_fp32_out(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                   B, Hq, Hkv, N, d, int(causal), float(scale), _stream(stream))
+    _check("fa_forward_fp32_out", code)
+    return o, lse
 
 
 def forward_f32(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None):

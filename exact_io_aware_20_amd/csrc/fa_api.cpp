@@ -151,6 +151,7 @@ fa::FwdParams fwd_params(const void* q, const void* k, const void* v, void* o, f
     p.block_mask = nullptr;
     p.scale = scale;
     p.scale_log2 = kernel_scale_log2(scale);
+    p.o32 = nullptr;
     return p;
 }
 
@@ -200,6 +201,21 @@ fa_status fa_forward(const void* q, const void* k, const void* v, void* o, float
     fa_status s = check_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, 2);
     if (s != FA_OK) return s;
     return launched(fa::launch_fwd_bf16(fwd_params(q, k, v, o, lse, B, Hq, Hkv, N, causal, scale), d, stream));
+}
+
+fa_status fa_forward_fp32_out(const void* q, const void* k, const void* v, float* o, float* lse, int B, int Hq,
+                              int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
+    // o holds fp32 elements: validated as a 4-byte output against bf16 inputs
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    fa_status s = check_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, 2);
+    if (s != FA_OK) return s;
+    const uintptr_t ob = (uintptr_t)B * Hq * N * d * 4, kb = (uintptr_t)B * Hkv * N * d * 2;
+    const Arg a[5] = {{q, (uintptr_t)B * Hq * N * d * 2, false}, {k, kb, false}, {v, kb, false}, {o, ob, true},
+                      {lse, (uintptr_t)B * Hq * N * 4, true}};
+    if ((s = check_tensors(a, 5)) != FA_OK) return s;
+    fa::FwdParams p = fwd_params(q, k, v, nullptr, lse, B, Hq, Hkv, N, causal, scale);
+    p.o32 = o;
+    return launched(fa::launch_fwd_bf16(p, d, stream));
 }
 
 fa_status fa_forward_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,

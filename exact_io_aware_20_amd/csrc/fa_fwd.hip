@@ -99,6 +99,33 @@ __device__ __forceinline__ void fwd_pv_a(const TrAddr<D>& va, const u32x4 (&pf)[
             for (int db = 0; db < D / 32; ++db) o[db] = mfma32x32x16(va.frag(db, 32 * kb + 16 * h2), pf[kb][h2], o[db]);
 }
 
+// Epilogue store of one query row (row index `row` of [B*Hq*N]): the lane's O^T
+// registers times inv = 1/l, rounded to bf16 (round to nearest even).  With the
+// validation pointer p.o32 set, the same fp32 products are stored unrounded instead.
+template <int D>
+__device__ __forceinline__ void store_o(const FwdParams& p, size_t row, const f32x16 (&o)[D / 32], float inv,
+                                        int hh) {
+    if (p.o32) {
+        float* Or = p.o32 + row * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *(f32x4*)(Or + 32 * db + 8 * g + 4 * hh) =
+                    f32x4{o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv};
+        return;
+    }
+    uint16_t* Or = (uint16_t*)p.o + row * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const u32x2 v2 = {pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                              pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+            *(u32x2*)(Or + 32 * db + 8 * g + 4 * hh) = v2;
+        }
+}
+
 // The kernel is software-pipelined by one tile: S(t+1) = K(t+1) Q^T goes to the
 // matrix cores while the vector units turn S(t) into probabilities.  LDS holds
 // K(t+1) and V(t) during step t; the direct loads of K(t+2) and V(t+1) fill the
@@ -299,16 +326,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
     // ---- epilogue: O = O^T / l (bf16, round to nearest even), LSE in natural log
     const float lt = l_part + __shfl_xor(l_part, 32);
     if (q < N) {
-        uint16_t* Oh = (uint16_t*)p.o + (size_t)head * N * D + (size_t)q * D;
-        const float inv = 1.0f / lt;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const u32x2 v2 = {pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
-                                  pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
-                *(u32x2*)(Oh + 32 * db + 8 * g + 4 * hh) = v2;
-            }
+        store_o<D>(p, (size_t)head * N + q, o, 1.0f / lt, hh);
         if (hh == 0) p.lse[(size_t)head * N + q] = (m_ref + __log2f(lt)) * kLn2;
     }
 }
@@ -531,16 +549,7 @@ void fa_fwd_persist_kernel(FwdParams p) {
         // epilogue of the finished item: O = O^T / l (bf16, RNE), LSE in natural log
         const float lt = l_part + __shfl_xor(l_part, 32);
         if (q < N) {
-            uint16_t* Oh = (uint16_t*)p.o + (size_t)cur.head * N * D + (size_t)q * D;
-            const float inv = 1.0f / lt;
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const u32x2 v2 = {pack_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
-                                      pack_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
-                    *(u32x2*)(Oh + 32 * db + 8 * g + 4 * hh) = v2;
-                }
+            store_o<D>(p, (size_t)cur.head * N + q, o, 1.0f / lt, hh);
             if (hh == 0) p.lse[(size_t)cur.head * N + q] = (m_ref + __log2f(lt)) * kLn2;
         }
         if (nitem < 0) break;

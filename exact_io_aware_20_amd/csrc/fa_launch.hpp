@@ -33,6 +33,8 @@ struct FwdParams {
     const uint8_t* block_mask;   // block-sparse layout [nb][nb] over 64 x 64 blocks, or null
     float scale;        // softmax scale
     float scale_log2;   // scale * log2(e)
+    float* o32;         // validation only: when set, the dense kernels store O in fp32 here
+                        // (the value they would round to bf16) instead of writing o
 };
 
 struct BwdParams {

@@ -91,6 +91,17 @@ fa_status fa_forward_f32(const float* q, const float* k, const float* v, float* 
                          int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                          hipStream_t stream);
 
+/*
+ * Validation diagnostic (not a production path): exactly fa_forward's kernel and
+ * arithmetic, but O is stored as fp32 [B,Hq,N,d] (the value fa_forward rounds to
+ * bf16), so a test can separate the kernel's own error from the bf16 rounding of the
+ * stored output: rounding this O to bf16 (nearest even) gives fa_forward's O bit for
+ * bit.  q, k, v bf16 as for fa_forward; lse as for fa_forward.  Same rules and errors.
+ */
+fa_status fa_forward_fp32_out(const void* q, const void* k, const void* v, float* o, float* lse,
+                              int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                              hipStream_t stream);
+
 /* Bytes of device workspace fa_backward needs: two fp32 per query row (the
  * per-row term D_i = sum_t dO_it * O_it, and LSE_i in base-2 units; lecture summary,
  * "推导 FlashAttention 的在线 softmax": the backward pass rebuilds P from the small

@@ -287,6 +287,9 @@ def test_every_entry_point_launches_only_after_validation():
     calls = [
         ("fa_forward", 1, lambda c: lib.fa_forward(Q, K, V, O, L, 2, 4, 2, 300, 128, c, 0.1, None),
          lambda: lib.fa_forward(Q, K, V, O, L, 2, 4, 2, 300, 96, 1, 0.1, None)),
+        ("fa_forward_fp32_out", 1, lambda c: lib.fa_forward_fp32_out(Q, K, V, O, L, 2, 4, 2, 300, 128, c, 0.1,
+                                                                      None),
+         lambda: lib.fa_forward_fp32_out(Q, K, V, L - 64, L, 2, 4, 2, 300, 128, 1, 0.1, None)),
         ("fa_forward_f32", 1, lambda c: lib.fa_forward_f32(Q, K, V, O, L, 2, 4, 2, 300, 64, c, 0.1, None),
          lambda: lib.fa_forward_f32(Q, K, V, Q, L, 2, 4, 2, 300, 64, 1, 0.1, None)),
         ("fa_backward", 3, lambda c: lib.fa_backward(Q, K, V, O, dO, L, dq, dk, dv, ws, need, 2, 4, 2, 300, 128, c,
