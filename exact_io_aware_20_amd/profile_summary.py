@@ -6,6 +6,7 @@ that bench.py reports beside its roofline.
     python -m exact_io_aware_20_amd.profile_summary mfma <pmc_dir> <out.md> <command>
     python -m exact_io_aware_20_amd.profile_summary states <pmc_dir> <out.md> <command>
     python -m exact_io_aware_20_amd.profile_summary lds <pmc_dir> <out.md> <command>
+    python -m exact_io_aware_20_amd.profile_summary valu <pmc_dir> <out.md> <command>
 
 `trace` turns a `--kernel-trace --stats` run into a table of per-kernel launch
 counts and durations.  `traffic` reads two `--pmc` runs (FETCH_SIZE, then
@@ -20,7 +21,9 @@ of SIMD cycles each attention kernel kept the matrix pipe busy.  `states` reads 
 run of the wave-state counters (STATE_COUNTERS) and splits each kernel's wave time
 into issuing, waiting at s_waitcnt or a barrier, and waiting for an issue slot or a
 dependency.  `lds` reads a run of LDS_COUNTERS and reports how busy the LDS was and
-the bytes per clock per CU it delivered to LDS loads.
+the bytes per clock per CU it delivered to LDS loads.  `valu` reads a run of
+VALU_COUNTERS and reports the share of each kernel's SIMD cycles that issuing its
+vector instructions takes (the secondary roofline of the softmax work).
 """
 from __future__ import annotations
 
@@ -315,6 +318,69 @@ def _write_lds_md(m, out, command):
         f.write("\n".join(lines) + "\n")
 
 
+VALU_COUNTERS = ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA", "SQ_ACTIVE_INST_VALU",
+                 "GRBM_GUI_ACTIVE")
+VALU_TAG = "valu-json:"
+# Issue cycles of one wave64 vector instruction on its SIMD (16 lanes, four passes) and of
+# one v_exp_f32 (measured back to back on gfx950 with a throughput probe: about 10).
+VALU_ISSUE_CYCLES = 4.0
+TRANS_ISSUE_CYCLES = 10.0
+
+
+def valu_load(pmc_dir: str) -> dict:
+    """Per attention kernel (means per dispatch): vector instructions other than MFMA,
+    the transcendental ones among them, MFMAs, and the share of the kernel's SIMD cycles
+    that issuing the vector instructions alone takes at the issue costs above:
+    (other x 4 + transcendental x 10) / (GRBM_GUI_ACTIVE / XCDs x SIMDs).  A share near 1
+    means the kernel is bound by vector issue, whatever its matrix work."""
+    agent = gpu_agent(pmc_dir)
+    out = {}
+    for k, v in _kernel_counters(pmc_dir, VALU_COUNTERS).items():
+        cycles = v["GRBM_GUI_ACTIVE"] / agent["xcc"]
+        if cycles <= 0:
+            continue
+        vec = v["SQ_INSTS_VALU"] - v["SQ_INSTS_MFMA"]
+        trans = v["SQ_INSTS_VALU_TRANS_F32"]
+        need = ((vec - trans) * VALU_ISSUE_CYCLES + trans * TRANS_ISSUE_CYCLES) / agent["simds"]
+        out[k] = {"valu": vec, "trans": trans, "mfma": v["SQ_INSTS_MFMA"], "cycles": cycles,
+                  "valu_issue_frac": need / cycles, "valu_per_mfma": vec / max(1.0, v["SQ_INSTS_MFMA"])}
+    return {"agent": agent, "kernels": out, "source_digest": source_digest()}
+
+
+def _write_valu_md(m, out, command):
+    a = m["agent"]
+    name = os.path.splitext(os.path.basename(out))[0].replace("valu_load_", "")
+    lines = [f"# Vector-ALU load: {name}", "", "One counter run (run from the repository root; `$R` is the repository path):",
+             "", f"    {command}", "",
+             "Means per dispatch. `vector` = SQ_INSTS_VALU - SQ_INSTS_MFMA (wave instructions), `exp` = "
+             f"SQ_INSTS_VALU_TRANS_F32; `issue share` = (non-exp x {VALU_ISSUE_CYCLES:g} + exp x "
+             f"{TRANS_ISSUE_CYCLES:g} cycles) / (GRBM_GUI_ACTIVE / {a['xcc']} XCDs x {a['simds']} SIMDs), the share "
+             "of the kernel's SIMD cycles that issuing its vector instructions alone takes (the secondary, "
+             f"vector-ALU roofline). Kernel sources digest: `{m['source_digest']}`.", "",
+             "| kernel | vector | exp | MFMA | vector per MFMA | issue share |", "|---|---|---|---|---|---|"]
+    for k, v in sorted(m["kernels"].items()):
+        lines.append(f"| {k} | {v['valu']:.4g} | {v['trans']:.4g} | {v['mfma']:.4g} | {v['valu_per_mfma']:.2f} | "
+                     f"{v['valu_issue_frac']:.3f} |")
+    lines += ["", VALU_TAG + " " + json.dumps(m)]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def committed_valu(md_path: str, kernel: str):
+    """The vector-ALU figures of `kernel` from a committed summary, or None when the file
+    is missing or the kernel sources changed since the counters were taken."""
+    if not os.path.exists(md_path):
+        return None
+    with open(md_path) as f:
+        for line in f:
+            if line.startswith(VALU_TAG):
+                data = json.loads(line[len(VALU_TAG):])
+                if data.get("source_digest") != source_digest():
+                    return None
+                return data["kernels"].get(kernel)
+    return None
+
+
 def main(argv):
     if len(argv) >= 5 and argv[0] == "trace":
         skip = int(argv[3])
@@ -327,6 +393,8 @@ def main(argv):
         _write_states_md(wave_states(argv[1]), argv[2], argv[3])
     elif len(argv) >= 4 and argv[0] == "lds":
         _write_lds_md(lds_use(argv[1]), argv[2], argv[3])
+    elif len(argv) >= 4 and argv[0] == "valu":
+        _write_valu_md(valu_load(argv[1]), argv[2], argv[3])
     else:
         raise SystemExit(__doc__)
 

@@ -100,3 +100,19 @@ def test_lds_use_per_cu(tmp_path):
     v = m["kernels"]["fa_fwd_bf16_kernel<128, false>"]
     assert abs(v["busy"] - 0.25) < 1e-12
     assert abs(v["load_bytes_per_clk_cu"] - 64.0) < 1e-12
+
+
+def test_valu_issue_share(tmp_path):
+    k = "void fa::fa_fwd_persist_kernel<64, false>(fa::FwdParams)"
+    # 8 XCDs x 1000 cycles on 1024 SIMDs; per SIMD 100 vector instructions (20 of them
+    # exp) besides 10 MFMAs: (80 x 4 + 20 x 10) / 1000 = 0.52 of the cycles
+    rows = [(k, "GRBM_GUI_ACTIVE", 8000), (k, "SQ_INSTS_VALU", 1024 * 110), (k, "SQ_INSTS_MFMA", 1024 * 10),
+            (k, "SQ_INSTS_VALU_TRANS_F32", 1024 * 20), (k, "SQ_ACTIVE_INST_VALU", 0)]
+    m = ps.valu_load(_counter_dir(tmp_path, "v", rows))
+    v = m["kernels"]["fa_fwd_persist_kernel<64, false>"]
+    assert abs(v["valu_issue_frac"] - 0.52) < 1e-12
+    assert abs(v["valu_per_mfma"] - 10.0) < 1e-12
+    md = tmp_path / "valu.md"
+    ps._write_valu_md(m, str(md), "cmd")
+    assert ps.committed_valu(str(md), "fa_fwd_persist_kernel<64, false>")["valu"] == 1024 * 100
+    assert ps.committed_valu(str(md), "missing") is None
