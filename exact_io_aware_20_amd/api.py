@@ -17,9 +17,10 @@ LIB_PATH = Path(os.environ.get("FA_MI355X_LIB", Path(__file__).resolve().parent 
 FA_STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_GQA", 4: "FA_ERR_HEADDIM",
     5: "FA_ERR_SCALE", 6: "FA_ERR_ALIGN", 7: "FA_ERR_FLAG", 8: "FA_ERR_WORKSPACE",
-    9: "FA_ERR_ALIAS", 10: "FA_ERR_LAUNCH", 11: "FA_ERR_WINDOW",
+    9: "FA_ERR_ALIAS", 10: "FA_ERR_LAUNCH", 11: "FA_ERR_WINDOW", 12: "FA_ERR_SCRATCH",
 }
 ENTRY_POINTS = ("fa_forward", "fa_forward_f32", "fa_forward_fp32_out", "fa_backward", "fa_backward_workspace_bytes",
+                "fa_backward_noalloc",
                 "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq",
                 "fa_decode_forward", "fa_decode_workspace_bytes", "fa_decode_split", "fa_decode_merge",
                 "fa_forward_window", "fa_backward_window", "fa_backward_dkdv_window", "fa_backward_dq_window",
@@ -54,6 +55,8 @@ def load_library() -> ctypes.CDLL:
     lib.fa_forward_fp32_out.restype = i
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
     lib.fa_backward.restype = i
+    lib.fa_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_backward_noalloc.restype = i
     lib.fa_backward_preprocess.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, vp]
     lib.fa_backward_preprocess.restype = i
     lib.fa_backward_dkdv.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, i, i, f, vp]
@@ -285,6 +288,28 @@ def backward(q, k, v, o, do, lse, causal: bool, scale: float, dq=None, dk=None, 
                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                             B, Hq, Hkv, N, d, int(causal), *extra, float(scale), _stream(stream))
     _check(fn, code)
+    return dq, dk, dv
+
+
+def backward_noalloc(q, k, v, o, do, lse, causal: bool, scale: float, dq=None, dk=None, dv=None, stream=None):
+    """bf16 backward via fa_backward_noalloc (no workspace: the library's static scratch,
+    at most 2^21 query rows).  Returns (dq, dk, dv)."""
+    lib = load_library()
+    B, Hq, Hkv, N, d = _shape(q, k)
+    for t, name, shp in ((q, "q", (B, Hq, N, d)), (k, "k", (B, Hkv, N, d)), (v, "v", (B, Hkv, N, d)),
+                         (o, "o", (B, Hq, N, d)), (do, "do", (B, Hq, N, d))):
+        _require(t, name, torch.bfloat16, shp)
+    _require(lse, "lse", torch.float32, (B, Hq, N))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _require(dq, "dq", torch.bfloat16, (B, Hq, N, d))
+    _require(dk, "dk", torch.bfloat16, (B, Hkv, N, d))
+    _require(dv, "dv", torch.bfloat16, (B, Hkv, N, d))
+    code = lib.fa_backward_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                   lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                   B, Hq, Hkv, N, d, int(causal), float(scale), _stream(stream))
+    _check("fa_backward_noalloc", code)
     return dq, dk, dv
 
 

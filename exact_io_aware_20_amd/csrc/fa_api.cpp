@@ -384,6 +384,28 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
     return launched(fa::launch_bwd_dq(p, d, stream));
 }
 
+fa_status fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                              const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+                              int causal, float scale, hipStream_t stream) {
+    // validated as fa_backward, except that the per-row workspace is the library's own
+    // static scratch (which no caller tensor can overlap)
+    fa_status s = check_shape(B, Hq, Hkv, N, d, causal, scale);
+    if (s != FA_OK) return s;
+    if ((long long)B * Hq * N > fa::kScratchRows) return FA_ERR_SCRATCH;
+    const uintptr_t qb = (uintptr_t)B * Hq * N * d * 2, kb = (uintptr_t)B * Hkv * N * d * 2;
+    const uintptr_t lb = (uintptr_t)B * Hq * N * 4;
+    const Arg a[9] = {{q, qb, false}, {k, kb, false}, {v, kb, false}, {o, qb, false}, {dO, qb, false},
+                      {lse, lb, false}, {dq, qb, true}, {dk, kb, true}, {dv, kb, true}};
+    if ((s = check_tensors(a, 9)) != FA_OK) return s;
+    if (fa::bwd_grid_max(B, Hq, Hkv, N, d) > kMaxGrid) return FA_ERR_SHAPE;
+    float* ws = nullptr;
+    if ((s = launched(fa::bwd_scratch(stream, &ws))) != FA_OK) return s;
+    const fa::BwdParams p = bwd_params(q, k, v, o, dO, lse, dq, dk, dv, ws, B, Hq, Hkv, N, causal, scale);
+    if ((s = launched(fa::launch_bwd_pre(p, d, stream))) != FA_OK) return s;
+    if ((s = launched(fa::launch_bwd_dkdv(p, d, stream))) != FA_OK) return s;
+    return launched(fa::launch_bwd_dq(p, d, stream));
+}
+
 fa_status fa_forward_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
                             int Hkv, int N, int d, int causal, int window, float scale, hipStream_t stream) {
     if (window < 0) return FA_ERR_WINDOW;
@@ -556,6 +578,8 @@ const char* fa_status_string(fa_status status) {
         case FA_ERR_ALIAS: return "an output overlaps an input or another output";
         case FA_ERR_LAUNCH: return "kernel launch failed";
         case FA_ERR_WINDOW: return "window must be >= 0";
+        case FA_ERR_SCRATCH:
+            return "B * Hq * N exceeds the 2^21 query rows of the no-allocation backward's static scratch";
     }
     return "unknown status";
 }

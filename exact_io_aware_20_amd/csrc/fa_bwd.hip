@@ -28,6 +28,8 @@
 //   * Masks: tile ranges and mask tests follow the visible band as in the forward
 //     (causal, full, sliding window); a block-sparse layout switches both kernels to
 //     compacted lists of the tiles their blocks see (SPARSE instantiations).
+#include <mutex>
+
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -576,6 +578,45 @@ void fa_bwd_dq_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------
+// ---------------------------------------------------------------------------------
+// Static scratch of the no-allocation backward: 2 x kScratchRows fp32 (D, then LSE in
+// base 2), 16 MiB held on every device the library runs on until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host it names a
+// stand-in, not device memory): its device address is looked up once per device,
+// with that device current, and kept.
+// ---------------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[2 * kScratchRows];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t bwd_scratch(hipStream_t stream, float** ptr) {
+    int dev = 0;
+    hipError_t e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = (float*)p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 template <int D>
 static hipError_t launch_pre(const BwdParams& p, hipStream_t stream) {
     const long long rows = (long long)p.B * p.Hq * p.N;

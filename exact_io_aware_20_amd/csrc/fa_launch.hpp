@@ -93,6 +93,11 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, hipStream_t stream);
 enum DecodeSteps { kDecodeSplit = 1, kDecodeMerge = 2 };
 hipError_t launch_decode(const DecodeParams& p, int d, int steps, bool paged, hipStream_t stream);
+// No-allocation backward: the per-row workspace (D and LSE in base 2) lives in a static
+// device array of kScratchRows rows per device.  bwd_scratch returns that array's address
+// on the device `stream` belongs to (looked up once per device).
+constexpr long long kScratchRows = 1LL << 21;
+hipError_t bwd_scratch(hipStream_t stream, float** ptr);
 hipError_t launch_bwd_pre(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t stream);

@@ -60,7 +60,8 @@ typedef enum fa_status {
     FA_ERR_WORKSPACE = 8,  /* workspace NULL, misaligned or too small            */
     FA_ERR_ALIAS = 9,      /* an output overlaps an input or another output     */
     FA_ERR_LAUNCH = 10,    /* hipGetLastError reported a launch failure          */
-    FA_ERR_WINDOW = 11     /* window is negative                                 */
+    FA_ERR_WINDOW = 11,    /* window is negative                                 */
+    FA_ERR_SCRATCH = 12    /* larger than the no-allocation entry point's scratch */
 } fa_status;
 
 /*
@@ -131,6 +132,25 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
                       void* workspace, size_t workspace_bytes,
                       int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                       hipStream_t stream);
+
+/*
+ * fa_backward for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): no workspace
+ * argument and no allocation of any kind.  The per-row terms (D and LSE in base 2,
+ * 8 bytes per query row) go to a static device array of the library, 2^21 query rows
+ * (16 MiB) on every device the library runs on, held until the process ends; calls with
+ * B*Hq*N above 2^21 return FA_ERR_SCRATCH and launch nothing.  The array's address on
+ * the stream's device is looked up on the first call on that device.  Every call on a
+ * device shares that device's array: two calls that overlap in time on one device
+ * (e.g. on two streams) race and give wrong gradients; calls on one stream, or
+ * otherwise ordered, are safe (each call overwrites every row it reads).  Results are
+ * bit-identical to fa_backward_preprocess + fa_backward_dkdv + fa_backward_dq.  Other
+ * arguments, rules and errors as for fa_backward.
+ */
+fa_status fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                              const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                              int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                              hipStream_t stream);
 
 /*
  * The three steps fa_backward enqueues, in this order (same sources as fa_backward:

@@ -5,6 +5,7 @@
 // whether a call reached the launch stage.  Test infrastructure; never part of the
 // product library.
 #include <atomic>
+#include <cstdint>
 
 #include "../../exact_io_aware_20_amd/csrc/fa_launch.hpp"
 
@@ -23,6 +24,11 @@ hipError_t launch_decode(const DecodeParams&, int, int, bool, hipStream_t) { ret
 hipError_t launch_bwd_pre(const BwdParams&, int, hipStream_t) { return counted(); }
 hipError_t launch_bwd_dkdv(const BwdParams&, int, hipStream_t) { return counted(); }
 hipError_t launch_bwd_dq(const BwdParams&, int, hipStream_t) { return counted(); }
+// a fixed, aligned stand-in address (never dereferenced: the launchers are stand-ins)
+hipError_t bwd_scratch(hipStream_t, float** ptr) {
+    *ptr = reinterpret_cast<float*>(uintptr_t{0x7f0000000000});
+    return hipSuccess;
+}
 }  // namespace fa
 
 extern "C" long long fa_stub_launches() { return g_launches.load(); }

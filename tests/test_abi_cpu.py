@@ -295,6 +295,9 @@ def test_every_entry_point_launches_only_after_validation():
         ("fa_backward", 3, lambda c: lib.fa_backward(Q, K, V, O, dO, L, dq, dk, dv, ws, need, 2, 4, 2, 300, 128, c,
                                                       0.1, None),
          lambda: lib.fa_backward(Q, K, V, O, dO, L, dq, dk, dv, ws, need - 1, 2, 4, 2, 300, 128, 1, 0.1, None)),
+        ("fa_backward_noalloc", 3, lambda c: lib.fa_backward_noalloc(Q, K, V, O, dO, L, dq, dk, dv, 2, 4, 2, 300,
+                                                                      128, c, 0.1, None),
+         lambda: lib.fa_backward_noalloc(Q, K, V, O, dO, L, dq, dk, dv, 8, 32, 32, 8193, 128, 1, 0.1, None)),
         ("fa_backward_preprocess", 1, lambda c: lib.fa_backward_preprocess(O, dO, L, ws, need, 2, 4, 300, 128, None),
          lambda: lib.fa_backward_preprocess(O, dO, L, O, need, 2, 4, 300, 128, None)),
         ("fa_backward_dkdv", 1, lambda c: lib.fa_backward_dkdv(Q, K, V, dO, ws, need, dk, dv, 2, 4, 2, 300, 64, c,
@@ -369,3 +372,18 @@ def test_every_entry_point_launches_only_after_validation():
         before = _launches()
         assert bad() != 0, name
         assert _launches() == before, name
+
+
+def test_noalloc_backward_rejects_before_launch():
+    lib = api.load_library()
+    dO, dq, dk, dv = 0x20_0000_0000, 0x30_0000_0000, 0x40_0000_0000, 0x50_0000_0000
+    call = lambda *ptrs, B=1, Hq=2, Hkv=1, N=16, d=64, causal=1, scale=0.1: lib.fa_backward_noalloc(
+        *ptrs, B, Hq, Hkv, N, d, causal, scale, None)
+    base = (Q, K, V, O, dO, L, dq, dk, dv)
+    assert call(*base, N=(1 << 21) // 2 + 1) == 12          # 2^21 + 2 query rows: over the scratch
+    assert call(*base, B=8, Hq=32, Hkv=8, N=8193) == 12     # 2^21 rows fit, 256 more do not
+    assert call(None, *base[1:]) == 1
+    assert call(*base, d=96) == 4
+    assert call(*base[:6], Q, dk, dv) == 9                  # dq aliases q
+    assert call(*base, scale=float("nan")) == 5
+    assert lib.fa_status_string(12).decode().startswith("B * Hq * N exceeds")
