@@ -21,7 +21,8 @@ FA_STATUS = {
 }
 ENTRY_POINTS = ("fa_forward", "fa_forward_f32", "fa_forward_fp32_out", "fa_backward", "fa_backward_workspace_bytes",
                 "fa_backward_noalloc",
-                "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq",
+                "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_backward_dkdv_dq",
+                "fa_backward_dq_convert", "fa_backward_fused", "fa_backward_fused_workspace_bytes",
                 "fa_decode_forward", "fa_decode_workspace_bytes", "fa_decode_split", "fa_decode_merge",
                 "fa_forward_window", "fa_backward_window", "fa_backward_dkdv_window", "fa_backward_dq_window",
                 "fa_decode_paged_forward", "fa_decode_paged_split", "fa_decode_paged_merge",
@@ -63,6 +64,14 @@ def load_library() -> ctypes.CDLL:
     lib.fa_backward_dkdv.restype = i
     lib.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, i, f, vp]
     lib.fa_backward_dq.restype = i
+    lib.fa_backward_dkdv_dq.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_backward_dkdv_dq.restype = i
+    lib.fa_backward_fused.argtypes = lib.fa_backward.argtypes
+    lib.fa_backward_fused.restype = i
+    lib.fa_backward_fused_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_backward_fused_workspace_bytes.restype = sz
+    lib.fa_backward_dq_convert.argtypes = [vp, sz, vp, i, i, i, i, f, vp]
+    lib.fa_backward_dq_convert.restype = i
     lib.fa_backward_workspace_bytes.argtypes = [i, i, i]
     lib.fa_backward_workspace_bytes.restype = sz
     lib.fa_decode_forward.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, vp]
@@ -258,10 +267,15 @@ def workspace_bytes(B: int, Hq: int, N: int) -> int:
     return int(load_library().fa_backward_workspace_bytes(B, Hq, N))
 
 
+def fused_workspace_bytes(B: int, Hq: int, N: int, d: int) -> int:
+    return int(load_library().fa_backward_fused_workspace_bytes(B, Hq, N, d))
+
+
 def backward(q, k, v, o, do, lse, causal: bool, scale: float, dq=None, dk=None, dv=None,
-             workspace=None, stream=None, window=None, block_mask=None):
-    """bf16 backward via fa_backward (or fa_backward_window when ``window`` is given, or
-    fa_backward_blocksparse with ``block_mask``).  Returns (dq, dk, dv)."""
+             workspace=None, stream=None, window=None, block_mask=None, fused: bool = False):
+    """bf16 backward via fa_backward (or fa_backward_window when ``window`` is given,
+    fa_backward_blocksparse with ``block_mask``, or the fused alternative
+    fa_backward_fused with ``fused=True``).  Returns (dq, dk, dv)."""
     lib = load_library()
     B, Hq, Hkv, N, d = _shape(q, k)
     for t, name, shp in ((q, "q", (B, Hq, N, d)), (k, "k", (B, Hkv, N, d)), (v, "v", (B, Hkv, N, d)),
@@ -274,10 +288,12 @@ def backward(q, k, v, o, do, lse, causal: bool, scale: float, dq=None, dk=None, 
     _require(dq, "dq", torch.bfloat16, (B, Hq, N, d))
     _require(dk, "dk", torch.bfloat16, (B, Hkv, N, d))
     _require(dv, "dv", torch.bfloat16, (B, Hkv, N, d))
-    nbytes = workspace_bytes(B, Hq, N)
+    if fused and (window is not None or block_mask is not None):
+        raise ValueError("the fused backward has no window or block-sparse form")
+    nbytes = fused_workspace_bytes(B, Hq, N, d) if fused else workspace_bytes(B, Hq, N)
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    fn = "fa_backward" if window is None else "fa_backward_window"
+    fn = "fa_backward_fused" if fused else ("fa_backward" if window is None else "fa_backward_window")
     extra = () if window is None else (int(window),)
     lay = ()
     if block_mask is not None:
@@ -315,8 +331,11 @@ def backward_noalloc(q, k, v, o, do, lse, causal: bool, scale: float, dq=None, d
 
 def backward_steps(q, k, v, o, do, lse, causal: bool, scale: float, dq, dk, dv, workspace,
                    stream=None, steps=("pre", "dkdv", "dq"), window=None, block_mask=None):
-    """Enqueue the named backward steps (fa_backward_preprocess / _dkdv / _dq, or the
-    _window forms of the last two when ``window`` is given) in order.
+    """Enqueue the named backward steps in order: "pre" (fa_backward_preprocess), then
+    "dkdv" and "dq" (fa_backward_dkdv / _dq, or their _window and _blocksparse forms), as
+    fa_backward runs them, or the fused alternative's "fused" and "convert"
+    (fa_backward_dkdv_dq, fa_backward_dq_convert; the workspace then needs
+    fused_workspace_bytes, and "pre" also zeroes its accumulator).
 
     Preallocated outputs and workspace are required; this is the form the benchmark
     uses to time each kernel on its own.
@@ -329,6 +348,14 @@ def backward_steps(q, k, v, o, do, lse, causal: bool, scale: float, dq, dk, dv, 
         if step == "pre":
             code = lib.fa_backward_preprocess(o.data_ptr(), do.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
                                               wsb, B, Hq, N, d, st)
+        elif step == "fused":
+            if window is not None or block_mask is not None:
+                raise ValueError("the fused backward has no window or block-sparse form")
+            code = lib.fa_backward_dkdv_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                                           workspace.data_ptr(), wsb, dk.data_ptr(), dv.data_ptr(),
+                                           B, Hq, Hkv, N, d, int(causal), float(scale), st)
+        elif step == "convert":
+            code = lib.fa_backward_dq_convert(workspace.data_ptr(), wsb, dq.data_ptr(), B, Hq, N, d, float(scale), st)
         elif step == "dkdv" and block_mask is not None:
             code = lib.fa_backward_dkdv_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
                                                     workspace.data_ptr(), wsb, dk.data_ptr(), dv.data_ptr(),

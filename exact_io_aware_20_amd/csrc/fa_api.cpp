@@ -13,10 +13,20 @@ constexpr long long kMaxGrid = 0x7fffffffLL;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Two fp32 per query row: D (dO . O) and LSE in base-2 units.
+// Backward workspace, by query row r of R = B*Hq*N:
+//   [0, 8R)                D_r (fp32), then LSE_r * log2(e) (fp32): all that fa_backward
+//                          and its dK/dV and dQ kernels use;
+//   [align256(8R), + 4dR)  the fused alternative's fp32 dQ accumulator [R][d] (zeroed
+//                          by the preprocess when the workspace has room for it, added
+//                          to by the fused kernel, read by the conversion to bf16).
 size_t bwd_ws_bytes(int B, int Hq, int N) {
     if (B < 1 || Hq < 1 || N < 1) return 0;
     return (size_t)B * Hq * N * 2 * sizeof(float);
+}
+size_t bwd_dqacc_offset(int B, int Hq, int N) { return (bwd_ws_bytes(B, Hq, N) + 255) & ~(size_t)255; }
+size_t bwd_fused_ws_bytes(int B, int Hq, int N, int d) {
+    if (B < 1 || Hq < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+    return bwd_dqacc_offset(B, Hq, N) + (size_t)B * Hq * N * d * sizeof(float);
 }
 
 fa_status check_shape(int B, int Hq, int Hkv, int N, int d, int causal, float scale) {
@@ -67,7 +77,10 @@ fa_status check_fwd(const void* q, const void* k, const void* v, const void* o, 
     return check_tensors(a, 5);
 }
 
-enum BwdStep { kAll, kPre, kDkdv, kDq };
+// kAll: a whole backward call; kPre: the preprocess; kDkdv, kDq: the two kernels of the
+// deterministic pair (they read only the small workspace); kFused: the fused dK/dV/dQ
+// kernel (adds into the dQ accumulator); kConvert: accumulator -> dq.
+enum BwdStep { kAll, kPre, kDkdv, kDq, kFused, kConvert };
 
 fa_status check_bwd(BwdStep step, const void* q, const void* k, const void* v, const void* o,
                     const void* dO, const void* lse, const void* dq, const void* dk, const void* dv,
@@ -76,25 +89,29 @@ fa_status check_bwd(BwdStep step, const void* q, const void* k, const void* v, c
     fa_status s = check_shape(B, Hq, Hkv, N, d, causal, scale);
     if (s != FA_OK) return s;
     if (fa::bwd_grid_max(B, Hq, Hkv, N, d) > kMaxGrid) return FA_ERR_SHAPE;
-    const size_t ws_need = bwd_ws_bytes(B, Hq, N);
+    const bool fused = step == kFused || step == kConvert;
+    const size_t ws_need = fused ? bwd_fused_ws_bytes(B, Hq, N, d) : bwd_ws_bytes(B, Hq, N);
     if (!workspace || !aligned16(workspace) || ws_bytes < ws_need) return FA_ERR_WORKSPACE;
     const uintptr_t qb = (uintptr_t)B * Hq * N * d * 2, kb = (uintptr_t)B * Hkv * N * d * 2;
     const uintptr_t lb = (uintptr_t)B * Hq * N * 4;
     Arg a[11];
     int n = 0;
-    a[n++] = {dO, qb, false};
-    a[n++] = {workspace, ws_need, step == kAll || step == kPre};
+    // the preprocess also zeroes the fused accumulator when the workspace has room for it
+    const size_t fused_need = bwd_fused_ws_bytes(B, Hq, N, d);
+    const size_t ws_extent = step == kPre && ws_bytes >= fused_need ? fused_need : ws_need;
+    a[n++] = {workspace, ws_extent, step == kAll || step == kPre || step == kFused};
+    if (step != kConvert) a[n++] = {dO, qb, false};
     if (step == kAll || step == kPre) {
         a[n++] = {o, qb, false};
         a[n++] = {lse, lb, false};
     }
-    if (step != kPre) {
+    if (step != kPre && step != kConvert) {
         a[n++] = {q, qb, false};
         a[n++] = {k, kb, false};
         a[n++] = {v, kb, false};
     }
-    if (step == kAll || step == kDq) a[n++] = {dq, qb, true};
-    if (step == kAll || step == kDkdv) {
+    if (step == kAll || step == kDq || step == kConvert) a[n++] = {dq, qb, true};
+    if (step == kAll || step == kDkdv || step == kFused) {
         a[n++] = {dk, kb, true};
         a[n++] = {dv, kb, true};
     }
@@ -170,6 +187,7 @@ fa::BwdParams bwd_params(const void* q, const void* k, const void* v, const void
     p.dv = dv;
     p.dsum = (float*)workspace;
     p.lse2 = (float*)workspace + (size_t)B * Hq * N;
+    p.dqacc = nullptr;   // set by the calls of the fused alternative
     p.B = B;
     p.Hq = Hq;
     p.Hkv = Hkv;
@@ -186,6 +204,20 @@ fa::BwdParams bwd_params(const void* q, const void* k, const void* v, const void
 int kernel_window(int window, int N) { return window < N - 1 ? window : -1; }
 
 fa_status launched(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+// The backward as fa_backward runs it: preprocess (D, LSE in base 2), then the dK/dV and
+// dQ kernels of the deterministic pair.
+fa_status pair_backward(const fa::BwdParams& p, int d, hipStream_t stream) {
+    fa_status s;
+    if ((s = launched(fa::launch_bwd_pre(p, d, stream))) != FA_OK) return s;
+    if ((s = launched(fa::launch_bwd_dkdv(p, d, stream))) != FA_OK) return s;
+    return launched(fa::launch_bwd_dq(p, d, stream));
+}
+
+// The fused alternative: the workspace's dQ accumulator follows the per-row terms.
+void set_fused_accumulator(fa::BwdParams& p, const void* workspace, int B, int Hq, int N) {
+    p.dqacc = (float*)((const char*)workspace + bwd_dqacc_offset(B, Hq, N));
+}
 
 }  // namespace
 
@@ -379,9 +411,28 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
                             N, d, causal, scale);
     if (s != FA_OK) return s;
     const fa::BwdParams p = bwd_params(q, k, v, o, dO, lse, dq, dk, dv, workspace, B, Hq, Hkv, N, causal, scale);
+    return pair_backward(p, d, stream);
+}
+
+size_t fa_backward_fused_workspace_bytes(int B, int Hq, int N, int d) { return bwd_fused_ws_bytes(B, Hq, N, d); }
+
+fa_status fa_backward_fused(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                            const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                            int B, int Hq, int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
+    fa_status s = check_bwd(kAll, q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N, d,
+                            causal, scale);
+    if (s != FA_OK) return s;
+    if (workspace_bytes < bwd_fused_ws_bytes(B, Hq, N, d)) return FA_ERR_WORKSPACE;
+    const uintptr_t qb = (uintptr_t)B * Hq * N * d * 2, kb = (uintptr_t)B * Hkv * N * d * 2;
+    const Arg a[10] = {{workspace, bwd_fused_ws_bytes(B, Hq, N, d), true}, {q, qb, false}, {k, kb, false},
+                       {v, kb, false}, {o, qb, false}, {dO, qb, false}, {lse, (uintptr_t)B * Hq * N * 4, false},
+                       {dq, qb, true}, {dk, kb, true}, {dv, kb, true}};
+    if ((s = check_tensors(a, 10)) != FA_OK) return s;
+    fa::BwdParams p = bwd_params(q, k, v, o, dO, lse, dq, dk, dv, workspace, B, Hq, Hkv, N, causal, scale);
+    set_fused_accumulator(p, workspace, B, Hq, N);
     if ((s = launched(fa::launch_bwd_pre(p, d, stream))) != FA_OK) return s;
-    if ((s = launched(fa::launch_bwd_dkdv(p, d, stream))) != FA_OK) return s;
-    return launched(fa::launch_bwd_dq(p, d, stream));
+    if ((s = launched(fa::launch_bwd_fused(p, d, stream))) != FA_OK) return s;
+    return launched(fa::launch_bwd_dq_convert(p, d, stream));
 }
 
 fa_status fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -426,9 +477,7 @@ fa_status fa_backward_window(const void* q, const void* k, const void* v, const 
     if (s != FA_OK) return s;
     fa::BwdParams p = bwd_params(q, k, v, o, dO, lse, dq, dk, dv, workspace, B, Hq, Hkv, N, causal, scale);
     p.window = kernel_window(window, N);
-    if ((s = launched(fa::launch_bwd_pre(p, d, stream))) != FA_OK) return s;
-    if ((s = launched(fa::launch_bwd_dkdv(p, d, stream))) != FA_OK) return s;
-    return launched(fa::launch_bwd_dq(p, d, stream));
+    return pair_backward(p, d, stream);
 }
 
 fa_status fa_backward_dkdv_window(const void* q, const void* k, const void* v, const void* dO, const void* workspace,
@@ -537,8 +586,9 @@ fa_status fa_backward_preprocess(const void* o, const void* dO, const float* lse
     fa_status s = check_bwd(kPre, nullptr, nullptr, nullptr, o, dO, lse, nullptr, nullptr, nullptr,
                             workspace, workspace_bytes, B, Hq, Hq, N, d, 0, 1.f);
     if (s != FA_OK) return s;
-    const fa::BwdParams p = bwd_params(nullptr, nullptr, nullptr, o, dO, lse, nullptr, nullptr, nullptr,
-                                       workspace, B, Hq, Hq, N, 0, 1.f);
+    fa::BwdParams p = bwd_params(nullptr, nullptr, nullptr, o, dO, lse, nullptr, nullptr, nullptr,
+                                 workspace, B, Hq, Hq, N, 0, 1.f);
+    if (workspace_bytes >= bwd_fused_ws_bytes(B, Hq, N, d)) set_fused_accumulator(p, workspace, B, Hq, N);
     return launched(fa::launch_bwd_pre(p, d, stream));
 }
 
@@ -562,6 +612,30 @@ fa_status fa_backward_dq(const void* q, const void* k, const void* v, const void
     const fa::BwdParams p =
         bwd_params(q, k, v, nullptr, dO, nullptr, dq, nullptr, nullptr, workspace, B, Hq, Hkv, N, causal, scale);
     return launched(fa::launch_bwd_dq(p, d, stream));
+}
+
+fa_status fa_backward_dkdv_dq(const void* q, const void* k, const void* v, const void* dO, void* workspace,
+                              size_t workspace_bytes, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+                              int causal, float scale, hipStream_t stream) {
+    fa_status s = check_bwd(kFused, q, k, v, nullptr, dO, nullptr, nullptr, dk, dv, workspace, workspace_bytes, B,
+                            Hq, Hkv, N, d, causal, scale);
+    if (s != FA_OK) return s;
+    fa::BwdParams p =
+        bwd_params(q, k, v, nullptr, dO, nullptr, nullptr, dk, dv, workspace, B, Hq, Hkv, N, causal, scale);
+    set_fused_accumulator(p, workspace, B, Hq, N);
+    return launched(fa::launch_bwd_fused(p, d, stream));
+}
+
+fa_status fa_backward_dq_convert(const void* workspace, size_t workspace_bytes, void* dq, int B, int Hq, int N,
+                                 int d, float scale, hipStream_t stream) {
+    if (!dq) return FA_ERR_NULL;
+    fa_status s = check_bwd(kConvert, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dq, nullptr, nullptr,
+                            workspace, workspace_bytes, B, Hq, Hq, N, d, 0, scale);
+    if (s != FA_OK) return s;
+    fa::BwdParams p = bwd_params(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dq, nullptr, nullptr,
+                                 workspace, B, Hq, Hq, N, 0, scale);
+    set_fused_accumulator(p, workspace, B, Hq, N);
+    return launched(fa::launch_bwd_dq_convert(p, d, stream));
 }
 
 const char* fa_status_string(fa_status status) {

@@ -46,12 +46,17 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x 
 template <int D>
 __global__ __launch_bounds__(kThreads) void fa_bwd_pre_kernel(const uint16_t* o, const uint16_t* dO,
                                                               const float* lse, float* dsum, float* lse2,
-                                                              long long rows) {
+                                                              float* dqacc, long long rows) {
     constexpr int LPR = D / 8;
     const long long gid = (long long)blockIdx.x * kThreads + threadIdx.x;
     const long long row = gid / LPR;
     const int sub = (int)(gid % LPR);
     float acc = 0.f;
+    if (dqacc && row < rows) {   // the fused backward's dQ accumulator starts at zero
+        f32x4* z = (f32x4*)(dqacc + row * D + 8 * sub);
+        z[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        z[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     if (row < rows) {
         const u32x4 a = ld_global16(o + row * D + 8 * sub);
         const u32x4 g = ld_global16(dO + row * D + 8 * sub);
@@ -390,6 +395,343 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         dkdv_role<D, false, SPARSE>(p, smem, list, n, wave, tid & 63);
 }
 
+
+// ---------------------------------------------------------------------------------
+// Fused dK/dV/dQ kernel.  A workgroup owns 128 keys of one KV head, as the dK/dV
+// kernel above, and also forms dQ = scale dS K for every item it visits: the dS tile
+// of the item (64 queries x 128 keys, bf16) goes to LDS, and every query row's dQ
+// contribution is added in fp32 to an accumulator in the workspace with vector
+// atomics (global_atomic_add_f32); a convert kernel scales it into bf16 dQ once all
+// key blocks are done.  So S and dP are formed once per (query, key) pair for all
+// three gradients: five contractions instead of the seven of the dK/dV + dQ pair.
+//
+// Roles: wave w < 4 (P/dV) and w + 4 (dS/dK) share a SIMD and own keys 32w..32w+31,
+// as before, but both now work on the same item, with two barriers per item:
+//   A  item it has landed (stage it & 1); the dS of item it-1 is complete.
+//   phase 1: P/dV forms S, P and writes P (bf16 fragments) to slot it & 1;
+//            dS/dK forms dQ of item it-1 (one 32 x 32 tile), then dP = dO V^T.
+//   B  P(it) is visible.
+//   phase 2: P/dV forms dV^T += dO^T P, then its dQ tile of item it-1;
+//            dS/dK reads P, forms dS = P (dP - D), writes dS over P in natural
+//            [key][query] layout, and dK^T += Q^T dS.
+// The dQ tile products read dS transposed (A operand: query rows, keys along k) and
+// the workgroup's K tile transposed (B operand: d columns, keys along k), both with
+// the transposing LDS read.  Two Q/dO stages, K (two 64-key tiles) and two P/dS slots
+// fit the LDS (129 KB at d = 128).  Items run over (query head of the group, query
+// tile), the tiles from last to first, so the workgroups of neighbouring key blocks
+// visit the same query tile together and its Q/dO reads and dQ atomics meet in L2.
+// Keys at or beyond N are masked like hidden pairs (P = 0, so dS = 0).
+// ---------------------------------------------------------------------------------
+template <int D>
+struct FusedCfg {
+    static constexpr int WAVES = 8;
+    static constexpr int THREADS = WAVES * kWave;
+    static constexpr int BK = 128;                        // keys per workgroup
+    static constexpr int BQ = 64;                         // query rows per item
+    static constexpr int DC = D / 16;
+    static constexpr int DB = D / 32;
+    static constexpr int NAT = SwzTile<D, 1>::ELEMS;      // one 64-row Q, dO or K tile (bf16 elements)
+    static constexpr int STAGE = 2 * NAT + 2 * BQ * 2;    // Q, dO, then LSE2 and D (fp32, BQ each)
+    static constexpr int KOFF = 2 * STAGE;                // K of the workgroup: two 64-key tiles
+    static constexpr int SOFF = KOFF + 2 * NAT;           // two P / dS slots
+    static constexpr int SLOT = BK * BQ;                  // bf16 elements of one slot
+    static constexpr int TOTAL = SOFF + 2 * SLOT;
+    static_assert(BK == kDkdvKeys, "launch plan and kernel disagree on the key tile");
+    static_assert(TOTAL * 2 <= 160 * 1024, "LDS budget");
+};
+
+// S for query half qb of an item: -inf where the query row is >= N, the key is >= N,
+// or the pair is outside the band (so that 2^(S*sl2 - LSE2) is exactly 0 there).
+__device__ __forceinline__ void fused_mask_half(f32x16& s, int qrow0, int key, int N, int wl, int wr) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int qq = qrow0 + 8 * (r >> 2) + (r & 3);
+        s[r] = (key < N && qq < N && qq >= key - wr && qq <= key + wl) ? s[r] : kNegInf;
+    }
+}
+
+// s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8) that waits for every LDS operation and for all but the n youngest vector
+// memory operations of the wave (they retire in issue order).
+constexpr int wait_lgkm0_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+constexpr int kDqAtomics = 16;   // atomic adds of one dQ tile (one per C register)
+
+// Workgroup barrier of the fused kernel.  Each wave first waits for its LDS writes and
+// for its direct loads of the next item, but not for the dQ atomics it issued after
+// those loads (`pending` of them): __syncthreads() would wait for those too (its fence
+// covers global memory), and the atomics, which nothing in the workgroup reads, would
+// then stall every item.  The empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void fused_barrier(bool pending) {
+    asm volatile("" ::: "memory");
+    if (pending)
+        __builtin_amdgcn_s_waitcnt(wait_lgkm0_vm(kDqAtomics));
+    else
+        __builtin_amdgcn_s_waitcnt(wait_lgkm0_vm(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+// Mid-item barrier: only LDS writes (the P of the item) must be complete; the next
+// item's direct loads and the dQ atomics stay in flight.
+__device__ __forceinline__ void fused_lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(wait_lgkm0_vm(63));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int D, bool PV>
+__device__ __forceinline__ void fused_role(const BwdParams& p, uint16_t* smem, int wave, int lane) {
+    using C = FusedCfg<D>;
+    using DS = SwzTile<64, 1>;   // dS tile: 64 key rows x 64 query columns
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+    const int N = p.N;
+    const int G = p.Hq / p.Hkv;
+
+    const int ntile_k = (N + C::BK - 1) / C::BK;
+    int head_kv, kt;
+    map_block(blockIdx.x, gridDim.x, ntile_k, p.B * p.Hkv, false, head_kv, kt, 4);
+    const int b = head_kv / p.Hkv;
+    const int hkv = head_kv % p.Hkv;
+    const int k0 = kt * C::BK;
+    const int pair = wave & 3;
+    const int kw0 = k0 + 32 * pair;
+    const int key = kw0 + l32;
+
+    const size_t kvoff = (size_t)head_kv * N * D;
+    // K (P/dV waves) or V (dS/dK waves) as B operands (lane: key, slots: 8 d)
+    const uint16_t* kv = (const uint16_t*)(PV ? p.k : p.v) + kvoff;
+    u32x4 bfr[C::DC];
+#pragma unroll
+    for (int c = 0; c < C::DC; ++c) bfr[c] = key < N ? ld_global16(kv + (size_t)key * D + 16 * c + 8 * hh) : zero_u4();
+    f32x16 acc[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) acc[db] = zero16();
+
+    const int wl = band_left(p), wr = band_right(p);
+    const int qt_start = max(0, k0 - wr) / C::BQ;
+    const int per_head = min(N - 1, k0 + C::BK - 1 + wl) / C::BQ + 1 - qt_start;
+    const int nitems = G * per_head;
+    const float sl2 = p.scale_log2;
+
+    // this wave's dQ tile of an item: queries 32 qh .. +31, d columns 32 dbq .. +31
+    // (d = 128: every wave one of the eight; d = 64: the four P/dV waves)
+    constexpr bool kAllWaves = D == 128;
+    const bool dq_wave = kAllWaves || PV;
+    const int qh = kAllWaves ? (wave >> 2) : (pair >> 1);
+    const int dbq = kAllWaves ? (wave & 3) : (pair & 1);
+
+    uint16_t* ktile = smem + C::KOFF;
+    uint16_t* slots = smem + C::SOFF;
+
+    TileDma<D, 1, C::WAVES> dma;
+    dma.init(wave, lane);
+    RowOffsets<D> ro;
+    ro.init(l32, hh);
+    TrOffsets<D> to;
+    to.init(lane);
+    TrColOffsets<64> dso;    // dS tile, query block qh
+    dso.init(lane, qh);
+    TrColOffsets<D> kco;     // K tile, d block dbq
+    kco.init(lane, dbq);
+
+    auto item_q0 = [&](int it) { return (qt_start + per_head - 1 - it % per_head) * C::BQ; };
+    auto item_row = [&](int it) { return (size_t)(b * p.Hq + hkv * G + it / per_head) * N + item_q0(it); };
+    auto issue_item = [&](int it) {
+        const int q0 = item_q0(it);
+        const size_t roff = item_row(it);
+        uint16_t* st = smem + (it & 1) * C::STAGE;
+        dma.issue((const uint16_t*)p.q + roff * D, N - q0, st, wave);
+        dma.issue((const uint16_t*)p.dO + roff * D, N - q0, st + C::NAT, wave);
+        // LSE2 (wave 0) and D (wave 1): 4 bytes per lane; rows >= N read row N-1
+        if (wave < 2) {
+            const float* src = (wave == 0 ? p.lse2 : p.dsum) + roff + min(lane, N - 1 - q0);
+            __builtin_amdgcn_global_load_lds(src, (lds_void*)(st + 2 * C::NAT + wave * 2 * C::BQ), 4, 0, 0);
+        }
+    };
+    auto active = [&](int q0) { return kw0 < N && q0 + C::BQ - 1 >= kw0 - wr && q0 <= kw0 + 31 + wl; };
+
+    // dQ tile of item j from its dS (slot j & 1) and the workgroup's K, added to the
+    // fp32 accumulator by exactly kDqAtomics atomic instructions (fused_barrier counts
+    // them): a row >= N has dS = 0, so its exact zero is added to row N-1 instead
+    auto dq_products = [&](int j) {
+        const uint16_t* dsl = slots + (j & 1) * C::SLOT;
+        f32x16 c = zero16();
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const TrColAddr<64> sa(dso, lds_addr(dsl + t * DS::ELEMS));
+            const TrColAddr<D> ka(kco, lds_addr(ktile + t * C::NAT));
+#pragma unroll
+            for (int kk = 0; kk < 64; kk += 16) c = mfma32x32x16(sa.frag(kk), ka.frag(kk), c);
+        }
+        const int q0 = item_q0(j);
+        const int qbase = q0 + 32 * qh + 4 * hh;
+        float* dst = p.dqacc + (item_row(j) - q0) * D + 32 * dbq + l32;   // row 0 of the head
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int qq = min(qbase + 8 * (r >> 2) + (r & 3), N - 1);
+            atomicAddNoRet(dst + (size_t)qq * D, c[r]);
+        }
+    };
+
+    if (nitems > 0) {
+        // the workgroup's K (both 64-key tiles; a tile past N reads row N-1, finite, and
+        // its dS is 0) with the first item
+        const uint16_t* kh = (const uint16_t*)p.k + kvoff;
+        dma.issue(kh + (size_t)k0 * D, N - k0, ktile, wave);
+        const int k1 = min(k0 + 64, N - 1);
+        dma.issue(kh + (size_t)k1 * D, max(1, N - (k0 + 64)), ktile + C::NAT, wave);
+        issue_item(0);
+    }
+    u32x4 bf[2][2];   // P/dV: P of the item (B fragments of dV), kept across the mid barrier
+    f32x16 x[2];      // dS/dK: dP of the item, kept across the mid barrier
+    for (int it = 0; it <= nitems; ++it) {
+        const bool have = it < nitems;
+        const int q0 = have ? item_q0(it) : 0;
+        const uint16_t* st = smem + (it & 1) * C::STAGE;
+        const float* lse2 = (const float*)(st + 2 * C::NAT);
+        const float* dvec = lse2 + C::BQ;
+        const bool act = have && active(q0);
+        uint32_t* pslot = (uint32_t*)(slots + (it & 1) * C::SLOT) + pair * 64 * 16;
+        // A: item it has landed (the dQ atomics of the previous iteration may still be in
+        // flight), dS(it-1) is written
+        fused_barrier(dq_wave && it >= 2);
+        if (it + 1 < nitems) issue_item(it + 1);
+        // ---- phase 1
+        if constexpr (PV) {
+            __builtin_amdgcn_s_setprio(2);
+            if (act) {
+                const bool mask = q0 < kw0 + 31 - wr || q0 + C::BQ > N || q0 + C::BQ - 1 > kw0 + wl || kw0 + 31 >= N;
+                {
+                    const RowAddr<D> ra(ro, lds_addr(st));
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb) x[qb] = qk_half<D>(ra, bfr, qb);
+                }
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    if (mask) fused_mask_half(x[qb], q0 + 32 * qb + 4 * hh, key, N, wl, wr);
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 L = *(const f32x4*)(lse2 + 32 * qb + 8 * g + 4 * hh);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            x[qb][4 * g + i] = fast_exp2(__builtin_fmaf(x[qb][4 * g + i], sl2, -L[i]));
+                    }
+                    pack_half(x[qb], bf[qb]);
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) *(u32x4*)(pslot + ((2 * qb + h2) * 64 + lane) * 4) = bf[qb][h2];
+                }
+            }
+            __builtin_amdgcn_s_setprio(0);
+        } else {
+            if (it > 0 && dq_wave) dq_products(it - 1);
+            if (act) {
+                const RowAddr<D> ra(ro, lds_addr(st + C::NAT));
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) x[qb] = qk_half<D>(ra, bfr, qb);
+            }
+        }
+        fused_lds_barrier();                                           // B: P(it) is written
+        // ---- phase 2
+        if constexpr (PV) {
+            if (act) {
+                const TrAddr<D> ta(to, lds_addr(st + C::NAT));
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) acc_half<D>(ta, bf[qb], acc, qb);   // dV^T += dO^T P
+            }
+            if (it > 0 && dq_wave) dq_products(it - 1);
+        } else {
+            uint16_t* dsrow = slots + (it & 1) * C::SLOT + (pair >> 1) * DS::ELEMS;
+            const int r = 32 * (pair & 1) + l32;   // this lane's key row in its 64-key dS tile
+            if (act) {
+                __builtin_amdgcn_s_setprio(2);
+                f32x16 pp[2];
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const u32x4 v = *(const u32x4*)(pslot + ((2 * qb + h2) * 64 + lane) * 4);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            // inverse of pack_half: word j of fragment h2 holds registers
+                            // r and r + 1, r = 4 (2 h2 + j/2) + 2 (j%2)
+                            const int rr = 4 * (2 * h2 + (j >> 1)) + 2 * (j & 1);
+                            pp[qb][rr] = bf16_lo(v[j]);
+                            pp[qb][rr + 1] = bf16_hi(v[j]);
+                        }
+                    }
+                u32x4 dsf[2][2];
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 Dd = *(const f32x4*)(dvec + 32 * qb + 8 * g + 4 * hh);
+                        float v[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) v[i] = pp[qb][4 * g + i] * (x[qb][4 * g + i] - Dd[i]);
+                        // registers 4g..4g+3: queries 32 qb + 8 g + 4 hh + 0..3; packed as
+                        // pack_half packs them (B fragment g/2, words 2(g%2), 2(g%2)+1), and
+                        // written to the natural [key][query] dS tile in one 8-byte store
+                        const uint32_t lo = pack_bf16(v[0], v[1]), hi = pack_bf16(v[2], v[3]);
+                        if (g == 0) { dsf[qb][0][0] = lo; dsf[qb][0][1] = hi; }
+                        if (g == 1) { dsf[qb][0][2] = lo; dsf[qb][0][3] = hi; }
+                        if (g == 2) { dsf[qb][1][0] = lo; dsf[qb][1][1] = hi; }
+                        if (g == 3) { dsf[qb][1][2] = lo; dsf[qb][1][3] = hi; }
+                        *(u32x2*)(dsrow + DS::at(r, 4 * qb + g) + 4 * hh) = u32x2{lo, hi};
+                    }
+                }
+                __builtin_amdgcn_s_setprio(0);
+                const TrAddr<D> ta(to, lds_addr(st));
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) acc_half<D>(ta, dsf[qb], acc, qb);   // dK^T += Q^T dS
+            } else if (have) {
+                // no key of this pair sees the item: its dS rows are zero
+#pragma unroll
+                for (int c = 0; c < 8; ++c) *(u32x2*)(dsrow + DS::at(r, c) + 4 * hh) = u32x2{0u, 0u};
+            }
+        }
+    }
+
+    if (key < N) {
+        uint16_t* dst = (uint16_t*)(PV ? p.dv : p.dk) + kvoff + (size_t)key * D;
+        const float sc = PV ? 1.f : p.scale;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *(u32x2*)(dst + 32 * db + 8 * g + 4 * hh) =
+                    u32x2{pack_bf16(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc),
+                          pack_bf16(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc)};
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(FusedCfg<D>::THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_fused_kernel(BwdParams p) {
+    using C = FusedCfg<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[C::TOTAL];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __builtin_assume(wave < C::WAVES);
+    if (wave < 4)
+        fused_role<D, true>(p, smem, wave, tid & 63);
+    else
+        fused_role<D, false>(p, smem, wave, tid & 63);
+}
+
+// dQ = scale * accumulator, rounded to bf16 (round to nearest even): 8 values per lane.
+template <int D>
+__global__ __launch_bounds__(kThreads) void fa_bwd_dq_convert_kernel(const float* dqacc, uint16_t* dq, float scale,
+                                                                     long long n8) {
+    const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= n8) return;
+    const f32x4 a = *(const f32x4*)(dqacc + 8 * i);
+    const f32x4 c = *(const f32x4*)(dqacc + 8 * i + 4);
+    *(u32x4*)(dq + 8 * i) = u32x4{pack_bf16(a[0] * scale, a[1] * scale), pack_bf16(a[2] * scale, a[3] * scale),
+                                  pack_bf16(c[0] * scale, c[1] * scale), pack_bf16(c[2] * scale, c[3] * scale)};
+}
+
 // ---------------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------------
@@ -622,7 +964,7 @@ static hipError_t launch_pre(const BwdParams& p, hipStream_t stream) {
     const long long rows = (long long)p.B * p.Hq * p.N;
     const unsigned blocks = (unsigned)((rows * (D / 8) + kThreads - 1) / kThreads);
     hipLaunchKernelGGL(fa_bwd_pre_kernel<D>, dim3(blocks), dim3(kThreads), 0, stream,
-                       (const uint16_t*)p.o, (const uint16_t*)p.dO, p.lse, p.dsum, p.lse2, rows);
+                       (const uint16_t*)p.o, (const uint16_t*)p.dO, p.lse, p.dsum, p.lse2, p.dqacc, rows);
     return hipGetLastError();
 }
 
@@ -645,6 +987,29 @@ static hipError_t launch_dq(const BwdParams& p, hipStream_t stream) {
     else
         hipLaunchKernelGGL((fa_bwd_dq_kernel<D, false>), dim3(blocks), dim3(DqCfg<D>::THREADS), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_fused(const BwdParams& p, hipStream_t stream) {
+    const unsigned blocks = (unsigned)((long long)p.B * p.Hkv * ((p.N + FusedCfg<D>::BK - 1) / FusedCfg<D>::BK));
+    hipLaunchKernelGGL((fa_bwd_fused_kernel<D>), dim3(blocks), dim3(FusedCfg<D>::THREADS), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_dq_convert(const BwdParams& p, hipStream_t stream) {
+    const long long n8 = (long long)p.B * p.Hq * p.N * D / 8;
+    const unsigned blocks = (unsigned)((n8 + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(fa_bwd_dq_convert_kernel<D>, dim3(blocks), dim3(kThreads), 0, stream, p.dqacc,
+                       (uint16_t*)p.dq, p.scale, n8);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_fused(const BwdParams& p, int d, hipStream_t stream) {
+    return d == 64 ? launch_fused<64>(p, stream) : launch_fused<128>(p, stream);
+}
+hipError_t launch_bwd_dq_convert(const BwdParams& p, int d, hipStream_t stream) {
+    return d == 64 ? launch_dq_convert<64>(p, stream) : launch_dq_convert<128>(p, stream);
 }
 
 hipError_t launch_bwd_pre(const BwdParams& p, int d, hipStream_t stream) {

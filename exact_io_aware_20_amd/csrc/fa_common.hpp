@@ -270,6 +270,33 @@ struct TrAddr {
     }
 };
 
+// The two tr_frag reads of one column block `db` chosen at run time (a wave-dependent
+// index into TrAddr's per-block array would force that array into scratch memory):
+// element offsets at kk = 0, then a per-tile opaque base as in TrAddr.
+template <int D>
+struct TrColOffsets {
+    uint32_t off[2];
+    __device__ __forceinline__ void init(int lane, int db) {
+        using S = SwzTile<D, 1>;
+        const int g = lane >> 4, m = lane & 15;
+        const int row = 4 * (g >> 1) + (m >> 2);
+        const int col = 32 * db + 16 * (g & 1) + 4 * (m & 3);
+        off[0] = (uint32_t)(S::at(row, col >> 3) + (col & 7));
+        off[1] = (uint32_t)(S::at(row + 8, col >> 3) + (col & 7));
+    }
+};
+template <int D>
+struct TrColAddr {
+    uint32_t a[2];
+    __device__ __forceinline__ TrColAddr(const TrColOffsets<D>& o, uint32_t base) {
+        a[0] = opaque(base + 2 * o.off[0]);
+        a[1] = opaque(base + 2 * o.off[1]);
+    }
+    __device__ __forceinline__ u32x4 frag(int kk) const {
+        return cat(tr_read_a(a[0] + 2 * kk * D), tr_read_a(a[1] + 2 * kk * D));
+    }
+};
+
 // ---------------------------------------------------------------------------------
 // Block-sparse layouts: a 0/1 byte matrix over 64 x 64 blocks of (query, key)
 // positions, nb x nb with nb = ceil(N / 64), shared by every (batch, head).  A

@@ -49,6 +49,8 @@ struct BwdParams {
     void* dv;
     float* dsum;        // workspace: D_i = dO_i . O_i, one fp32 per query row
     float* lse2;        // workspace: LSE_i * log2(e), one fp32 per query row
+    float* dqacc;       // workspace: fp32 dQ accumulator [B*Hq*N][d] of the fused backward
+                        // (zeroed by the preprocess when set), or null
     int B, Hq, Hkv, N, causal;
     int window;         // as in FwdParams
     const uint8_t* block_mask;   // as in FwdParams
@@ -100,6 +102,8 @@ constexpr long long kScratchRows = 1LL << 21;
 hipError_t bwd_scratch(hipStream_t stream, float** ptr);
 hipError_t launch_bwd_pre(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t stream);
+hipError_t launch_bwd_fused(const BwdParams& p, int d, hipStream_t stream);
+hipError_t launch_bwd_dq_convert(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t stream);
 
 }  // namespace fa

@@ -45,10 +45,17 @@ def bwd_bytes(B, Hq, Hkv, N, d, elt: int) -> int:
         + elt * (q_sized + 2 * kv_sized) + 3 * 2 * 4 * B * Hq * N
 
 
-def preprocess_bytes(B, Hq, N, d, elt: int) -> int:
+def preprocess_bytes(B, Hq, N, d, elt: int, zero_acc: bool = False) -> int:
     """The backward preprocess reads O, dO and the fp32 LSE and writes two fp32 per row
-    (D and LSE in base 2)."""
-    return 2 * elt * B * Hq * N * d + 3 * 4 * B * Hq * N
+    (D and LSE in base 2), and for the fused backward zeroes the fp32 dQ accumulator
+    (d values per row)."""
+    return 2 * elt * B * Hq * N * d + 3 * 4 * B * Hq * N + (4 * B * Hq * N * d if zero_acc else 0)
+
+
+def dq_convert_bytes(B, Hq, N, d, elt: int) -> int:
+    """The conversion of the fused backward's fp32 dQ accumulator to the output dtype:
+    reads d fp32 values per query row, writes d elements."""
+    return (4 + elt) * B * Hq * N * d
 
 
 def score_matrix_bytes(N, elt: int = 4, heads: int = 1, batch: int = 1) -> int:

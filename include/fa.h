@@ -103,10 +103,11 @@ fa_status fa_forward_fp32_out(const void* q, const void* k, const void* v, float
                               int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                               hipStream_t stream);
 
-/* Bytes of device workspace fa_backward needs: two fp32 per query row (the
- * per-row term D_i = sum_t dO_it * O_it, and LSE_i in base-2 units; lecture summary,
- * "推导 FlashAttention 的在线 softmax": the backward pass rebuilds P from the small
- * saved statistic).  Returns 0 for invalid sizes (B, Hq or N < 1). */
+/* Bytes of device workspace fa_backward needs: two fp32 per query row r of
+ * R = B*Hq*N (the per-row term D_r = sum_t dO_rt * O_rt, then LSE_r in base-2 units;
+ * lecture summary, "推导 FlashAttention 的在线 softmax": the backward pass rebuilds P
+ * from the small saved statistic), 8*R bytes.  Returns 0 for invalid sizes (B, Hq or
+ * N < 1). */
 size_t fa_backward_workspace_bytes(int B, int Hq, int N);
 
 /*
@@ -124,6 +125,8 @@ size_t fa_backward_workspace_bytes(int B, int Hq, int N);
  * dk and dv of a KV head are the sums over the Hq/Hkv query heads of its group.
  * workspace: device memory of at least fa_backward_workspace_bytes(B,Hq,N)
  * bytes (passed in workspace_bytes), 16-byte aligned, clobbered by the call.
+ * It enqueues fa_backward_preprocess, fa_backward_dkdv and fa_backward_dq; every
+ * output is bit-reproducible from run to run.
  * Errors: those of fa_forward, and FA_ERR_WORKSPACE (NULL, misaligned or smaller
  * than required); the workspace may overlap no tensor argument (FA_ERR_ALIAS).
  */
@@ -132,6 +135,28 @@ fa_status fa_backward(const void* q, const void* k, const void* v, const void* o
                       void* workspace, size_t workspace_bytes,
                       int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                       hipStream_t stream);
+
+/*
+ * Alternative backward with the same definition, arguments and results as fa_backward
+ * (code-corey Q38, section 2.(2) 重计算: recompute instead of store; here S and dP are
+ * formed once per (query, key) pair for all three gradients).  One kernel forms dK,
+ * dV and dQ: each query row's dQ contribution of a key block is added in fp32 with
+ * atomic adds to an accumulator in the workspace, which a last kernel scales into bf16
+ * dq.  Five contractions per pair instead of fa_backward's seven, but on MI355X the
+ * fp32 atomic traffic (4 bytes per query row, d and key block of 128) makes it slower
+ * than fa_backward at the sizes measured; dk and dv are bit-reproducible, dq may differ
+ * in its last bits from run to run (the order of the fp32 adds is not fixed).
+ * workspace: at least fa_backward_fused_workspace_bytes(B,Hq,N,d) bytes: the
+ * per-row terms of fa_backward, then from the next 256-byte boundary the fp32 dQ
+ * accumulator [B*Hq*N][d].  Enqueues fa_backward_preprocess, fa_backward_dkdv_dq and
+ * fa_backward_dq_convert.  Other rules and errors as for fa_backward.
+ */
+size_t fa_backward_fused_workspace_bytes(int B, int Hq, int N, int d);
+fa_status fa_backward_fused(const void* q, const void* k, const void* v, const void* o,
+                            const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                            void* workspace, size_t workspace_bytes,
+                            int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                            hipStream_t stream);
 
 /*
  * fa_backward for callers that cannot allocate device memory (code under HIP graph
@@ -153,20 +178,25 @@ fa_status fa_backward_noalloc(const void* q, const void* k, const void* v, const
                               hipStream_t stream);
 
 /*
- * The three steps fa_backward enqueues, in this order (same sources as fa_backward:
- * the preprocess forms the per-row term of the softmax Jacobian, D_i = dO_i . O_i;
- * the other two recompute P from the saved statistic), exposed so that a caller
- * can place them itself (after fa_backward_preprocess, fa_backward_dkdv and
- * fa_backward_dq only read the workspace and may run concurrently on two
- * streams).  Arguments, layouts and errors are those of fa_backward.
+ * The backward's steps (same sources as fa_backward: the preprocess forms the per-row
+ * term of the softmax Jacobian, D_i = dO_i . O_i; the others recompute P from the saved
+ * statistic), exposed so that a caller can place and time them itself.  Arguments,
+ * layouts and errors are those of fa_backward.
  *   fa_backward_preprocess: for every query row (b, h, i), row index
- *     r = (b*Hq + h)*N + i, workspace as fp32 [2][B*Hq*N]:
+ *     r = (b*Hq + h)*N + i, workspace as fp32 [2][B*Hq*N] at its start:
  *     workspace[r] = D_r = sum_t dO_r,t * O_r,t and
- *     workspace[B*Hq*N + r] = lse[r] * log2(e).
- *   fa_backward_dkdv: dk, dv from q, k, v, dO and the preprocessed workspace.
- *   fa_backward_dq:   dq from q, k, v, dO and the preprocessed workspace.
- * The last two read the saved statistic only through the workspace, so it must
- * come from fa_backward_preprocess of the same o, dO and lse.
+ *     workspace[B*Hq*N + r] = lse[r] * log2(e); when workspace_bytes is at least
+ *     fa_backward_fused_workspace_bytes(B,Hq,N,d), it also zeroes the fused
+ *     alternative's dQ accumulator.
+ *   fa_backward_dkdv: dk, dv from q, k, v, dO and the preprocessed workspace;
+ *   fa_backward_dq:   dq from q, k, v, dO and the preprocessed workspace
+ *     (these two only read the workspace and may run concurrently on two streams).
+ *   fa_backward_dkdv_dq (fused alternative, workspace of
+ *     fa_backward_fused_workspace_bytes): dk, dv, and every row's dQ contribution added
+ *     (unscaled, fp32) into the accumulator, which it requires zeroed by the preprocess;
+ *   fa_backward_dq_convert: dq = scale * accumulator, rounded to bf16.
+ * The kernels after the preprocess read the saved statistic only through the
+ * workspace, so it must come from fa_backward_preprocess of the same o, dO and lse.
  */
 fa_status fa_backward_preprocess(const void* o, const void* dO, const float* lse, void* workspace,
                                  size_t workspace_bytes, int B, int Hq, int N, int d, hipStream_t stream);
@@ -178,6 +208,12 @@ fa_status fa_backward_dq(const void* q, const void* k, const void* v, const void
                          const void* workspace, size_t workspace_bytes,
                          void* dq, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                          hipStream_t stream);
+fa_status fa_backward_dkdv_dq(const void* q, const void* k, const void* v, const void* dO,
+                              void* workspace, size_t workspace_bytes, void* dk, void* dv,
+                              int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                              hipStream_t stream);
+fa_status fa_backward_dq_convert(const void* workspace, size_t workspace_bytes, void* dq,
+                                 int B, int Hq, int N, int d, float scale, hipStream_t stream);
 
 /*
  * Sliding-window attention: as fa_forward / fa_backward (and its dK/dV and dQ
@@ -206,6 +242,7 @@ fa_status fa_backward_dq_window(const void* q, const void* k, const void* v, con
                                 const void* workspace, size_t workspace_bytes,
                                 void* dq, int B, int Hq, int Hkv, int N, int d, int causal,
                                 int window, float scale, hipStream_t stream);
+
 
 /*
  * Block-sparse attention: as fa_forward / fa_backward (and its dK/dV and dQ steps),

@@ -71,7 +71,14 @@ def test_status_strings():
 
 def test_workspace_bytes():
     lib = api.load_library()
-    assert lib.fa_backward_workspace_bytes(2, 32, 8192) == 2 * 4 * 2 * 32 * 8192
+    rows = 2 * 32 * 8192
+    # D and LSE in base 2: 8 bytes per row
+    assert lib.fa_backward_workspace_bytes(2, 32, 8192) == 8 * rows
+    # the fused alternative: the same, then from a 256-byte boundary an fp32 dQ
+    # accumulator of d values per row
+    assert lib.fa_backward_fused_workspace_bytes(2, 32, 8192, 128) == 8 * rows + 512 * rows
+    assert lib.fa_backward_fused_workspace_bytes(1, 1, 3, 64) == 256 + 256 * 3
+    assert lib.fa_backward_fused_workspace_bytes(1, 1, 3, 96) == 0
     assert lib.fa_backward_workspace_bytes(0, 1, 1) == 0
     assert lib.fa_backward_workspace_bytes(1, 1, -5) == 0
 
@@ -248,7 +255,8 @@ def test_blocksparse_calls_reject_before_launch():
                                        None) == 1
     assert lib.fa_backward_blocksparse(Q, K, V, O, dO, L, dq, dk, dv, dq, ws, need, 1, 2, 1, 16, 64, 1, 0.1,
                                        None) == 9
-    assert lib.fa_backward_dkdv_blocksparse(Q, K, V, dO, ws, need - 4, dk, dv, BM, 1, 2, 1, 16, 64, 1, 0.1,
+    small = 8 * 2 * 16   # the dK/dV step reads only D and LSE in base 2
+    assert lib.fa_backward_dkdv_blocksparse(Q, K, V, dO, ws, small - 4, dk, dv, BM, 1, 2, 1, 16, 64, 1, 0.1,
                                             None) == 8
     assert lib.fa_backward_dq_blocksparse(Q, K, V, dO, ws, need, dq, BM, 1, 3, 2, 16, 64, 1, 0.1, None) == 3
 
@@ -281,6 +289,7 @@ def test_every_entry_point_launches_only_after_validation():
                               0x80_0000_0000)
     KP, VP, TB, SL = 0x70_0000_0000, 0x71_0000_0000, 0x72_0000_0000, 0x73_0000_0000
     need = lib.fa_backward_workspace_bytes(2, 4, 300)
+    fneed = lib.fa_backward_fused_workspace_bytes(2, 4, 300, 128)
     dneed = lib.fa_decode_workspace_bytes(2, 4, 2, 3, 1000, 128)
     # (name, launcher calls when valid (decode: one call covers its split and merge),
     #  valid call, a rejected variant)
@@ -306,6 +315,14 @@ def test_every_entry_point_launches_only_after_validation():
         ("fa_backward_dq", 1, lambda c: lib.fa_backward_dq(Q, K, V, dO, ws, need, dq, 2, 4, 2, 300, 64, c, 0.1,
                                                             None),
          lambda: lib.fa_backward_dq(Q, K, V, dO, ws, need, dq, 2, 4, 3, 300, 64, 1, 0.1, None)),
+        ("fa_backward_fused", 3, lambda c: lib.fa_backward_fused(Q, K, V, O, dO, L, dq, dk, dv, ws, fneed, 2, 4, 2,
+                                                                  300, 128, c, 0.1, None),
+         lambda: lib.fa_backward_fused(Q, K, V, O, dO, L, dq, dk, dv, ws, need, 2, 4, 2, 300, 128, 1, 0.1, None)),
+        ("fa_backward_dkdv_dq", 1, lambda c: lib.fa_backward_dkdv_dq(Q, K, V, dO, ws, fneed, dk, dv, 2, 4, 2, 300,
+                                                                      128, c, 0.1, None),
+         lambda: lib.fa_backward_dkdv_dq(Q, K, V, dO, ws, need, dk, dv, 2, 4, 2, 300, 128, 1, 0.1, None)),
+        ("fa_backward_dq_convert", 1, lambda c: lib.fa_backward_dq_convert(ws, fneed, dq, 2, 4, 300, 128, 0.1, None),
+         lambda: lib.fa_backward_dq_convert(ws, fneed, ws + 64, 2, 4, 300, 128, 0.1, None)),
         ("fa_forward_window", 1, lambda c: lib.fa_forward_window(Q, K, V, O, L, 2, 4, 2, 300, 128, c, 17, 0.1,
                                                                   None),
          lambda: lib.fa_forward_window(Q, K, V, O, L, 2, 4, 2, 300, 128, 1, -2, 0.1, None)),
@@ -362,7 +379,7 @@ def test_every_entry_point_launches_only_after_validation():
     named = {c[0] for c in calls}
     computing = {n for n in declared_functions()
                  if n not in ("fa_backward_workspace_bytes", "fa_decode_workspace_bytes", "fa_check_args",
-                              "fa_status_string")}
+                              "fa_status_string", "fa_backward_fused_workspace_bytes")}
     assert computing <= named, sorted(computing - named)
     for name, n_launch, ok, bad in calls:
         for causal in (0, 1):
@@ -387,3 +404,19 @@ def test_noalloc_backward_rejects_before_launch():
     assert call(*base[:6], Q, dk, dv) == 9                  # dq aliases q
     assert call(*base, scale=float("nan")) == 5
     assert lib.fa_status_string(12).decode().startswith("B * Hq * N exceeds")
+
+
+def test_fused_steps_need_the_accumulator():
+    lib = api.load_library()
+    dO, ws, dq, dk, dv = 0x20_0000_0000, 0x60_0000_0000, 0x30_0000_0000, 0x40_0000_0000, 0x50_0000_0000
+    small = lib.fa_backward_workspace_bytes(1, 2, 16)
+    full = lib.fa_backward_fused_workspace_bytes(1, 2, 16, 64)
+    # the fused steps and the fused whole call need the accumulator after the per-row terms
+    assert lib.fa_backward_fused(Q, K, V, O, dO, L, dq, dk, dv, ws, full - 1, 1, 2, 1, 16, 64, 1, 0.1, None) == 8
+    assert lib.fa_backward_dkdv_dq(Q, K, V, dO, ws, small, dk, dv, 1, 2, 1, 16, 64, 1, 0.1, None) == 8
+    assert lib.fa_backward_dkdv_dq(Q, K, V, dO, ws, full - 1, dk, dv, 1, 2, 1, 16, 64, 1, 0.1, None) == 8
+    assert lib.fa_backward_dq_convert(ws, full - 1, dq, 1, 2, 16, 64, 0.1, None) == 8
+    assert lib.fa_backward_dq_convert(ws, full, None, 1, 2, 16, 64, 0.1, None) == 1
+    assert lib.fa_backward_dq_convert(ws, full, dq, 1, 2, 16, 64, float("nan"), None) == 5
+    # the fused kernel writes the accumulator: it may not overlap an input
+    assert lib.fa_backward_dkdv_dq(Q, K, V, dO, Q - 64, full, dk, dv, 1, 2, 1, 16, 64, 1, 0.1, None) == 9

@@ -135,14 +135,19 @@ BWD_SMALL = [(1, 1, 1, 1, 64), (1, 2, 1, 3, 128), (2, 2, 2, 17, 64), (1, 4, 1, 6
              (1, 6, 2, 129, 64), (1, 4, 2, 200, 128), (1, 2, 2, 257, 64), (1, 3, 1, 384, 128)]
 
 
+@pytest.mark.parametrize("path", ["fused", "pair"])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("shape", BWD_SMALL, ids=lambda s: "x".join(map(str, s)))
-def test_backward_bf16_small(shape, causal):
+def test_backward_bf16_small(shape, causal, path):
+    # "pair": fa_backward (preprocess, dK/dV kernel, dQ kernel); "fused": the alternative
+    # fa_backward_fused (dK/dV and dQ in one kernel, dQ by fp32 atomic adds)
     B, Hq, Hkv, N, d = shape
     host, g = make(*shape, seed=9000 + N + d, with_do=True)
     scale = 1.0 / math.sqrt(d)
     o, lse = api.forward(g["q"], g["k"], g["v"], causal, scale)
-    dq, dk, dv = api.backward(g["q"], g["k"], g["v"], o, g["do"], lse, causal, scale)
+    dq, dk, dv = (torch.full_like(g[n], float("nan")) for n in ("q", "k", "v"))
+    api.backward(g["q"], g["k"], g["v"], o, g["do"], lse, causal, scale, dq=dq, dk=dk, dv=dv,
+                 fused=path == "fused")
     torch.cuda.synchronize()
     dq_r, dk_r, dv_r = oracle.attention_backward(host["q"], host["k"], host["v"], host["do"], causal, scale)
     for name, a, r in (("dq", dq, dq_r), ("dk", dk, dk_r), ("dv", dv, dv_r)):
@@ -399,34 +404,68 @@ def test_backward_whole_tensor_xcd_remap(shape, causal):
                 assert rel_l2(a[b, h], r[b, h]) <= 1e-2, (name, b, h, rel_l2(a[b, h], r[b, h]))
 
 
-def test_backward_steps_match_fused_call():
-    # the three entry points fa_backward enqueues, called one by one (dK/dV and dQ on
-    # two streams after the preprocess), give bit-identical gradients
+def test_backward_steps_match_whole_call():
+    # fa_backward equals its three steps called one by one, with dK/dV and dQ on two
+    # streams after the preprocess, bit for bit; the fused alternative equals its own
+    # steps (dK and dV bit for bit, dQ up to the order of its fp32 atomic adds)
     B, Hq, Hkv, N, d = 1, 4, 2, 300, 128
     host, g = make(B, Hq, Hkv, N, d, seed=9950, with_do=True)
     o, lse = api.forward(g["q"], g["k"], g["v"], True, 0.09)
     dq, dk, dv = api.backward(g["q"], g["k"], g["v"], o, g["do"], lse, True, 0.09)
-    dq2, dk2, dv2 = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
     ws = torch.empty(api.workspace_bytes(B, Hq, N), dtype=torch.uint8, device=dev())
-    api.backward_steps(g["q"], g["k"], g["v"], o, g["do"], lse, True, 0.09, dq2, dk2, dv2, ws, steps=("pre",))
+    p2 = [torch.empty_like(t) for t in (dq, dk, dv)]
+    api.backward_steps(g["q"], g["k"], g["v"], o, g["do"], lse, True, 0.09, *p2, ws, steps=("pre",))
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     s1.wait_stream(torch.cuda.current_stream())
     s2.wait_stream(torch.cuda.current_stream())
-    api.backward_steps(g["q"], g["k"], g["v"], o, g["do"], lse, True, 0.09, dq2, dk2, dv2, ws, stream=s1,
-                       steps=("dkdv",))
-    api.backward_steps(g["q"], g["k"], g["v"], o, g["do"], lse, True, 0.09, dq2, dk2, dv2, ws, stream=s2,
-                       steps=("dq",))
+    api.backward_steps(g["q"], g["k"], g["v"], o, g["do"], lse, True, 0.09, *p2, ws, stream=s1, steps=("dkdv",))
+    api.backward_steps(g["q"], g["k"], g["v"], o, g["do"], lse, True, 0.09, *p2, ws, stream=s2, steps=("dq",))
     torch.cuda.synchronize()
-    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+    for a, b in zip((dq, dk, dv), p2):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    f1 = api.backward(g["q"], g["k"], g["v"], o, g["do"], lse, True, 0.09, fused=True)
+    wsf = torch.empty(api.fused_workspace_bytes(B, Hq, N, d), dtype=torch.uint8, device=dev())
+    f2 = [torch.empty_like(t) for t in (dq, dk, dv)]
+    api.backward_steps(g["q"], g["k"], g["v"], o, g["do"], lse, True, 0.09, *f2, wsf,
+                       steps=("pre", "fused", "convert"))
+    torch.cuda.synchronize()
+    assert torch.equal(f1[1].view(torch.int16), f2[1].view(torch.int16))
+    assert torch.equal(f1[2].view(torch.int16), f2[2].view(torch.int16))
+    assert rel_l2(f64(f2[0]), f64(f1[0])) <= 1e-3
+
+
+def test_fused_backward_full_size():
+    # the fused alternative at the headline size: every element against the oracle
+    # through the same per-unit bar, and dK/dV bit-identical from run to run
+    w = inputs.WORKLOADS["causal_n8192_d128"]
+    host = inputs.workload_inputs(w)
+    g = {k: v.to(dev()) for k, v in host.items()}
+    o, lse = api.forward(g["q"], g["k"], g["v"], True, w.scale)
+    runs = []
+    for _ in range(2):
+        out = [poisoned(g[n].shape, torch.bfloat16) for n in ("q", "k", "v")]
+        api.backward(g["q"], g["k"], g["v"], o, g["do"], lse, True, w.scale, *out, fused=True)
+        runs.append(out)
+    torch.cuda.synchronize()
+    all_finite(dq=runs[0][0], dk=runs[0][1], dv=runs[0][2])
+    assert torch.equal(runs[0][1].view(torch.int16), runs[1][1].view(torch.int16))
+    assert torch.equal(runs[0][2].view(torch.int16), runs[1][2].view(torch.int16))
+    refs = oracle.attention_backward(host["q"], host["k"], host["v"], host["do"], True, w.scale, workers=WORKERS)
+    for name, a, r in zip(("dq", "dk", "dv"), runs[0], refs):
+        a = f64(a)
+        worst = max(rel_l2(a[b, h], r[b, h]) for b in range(a.shape[0]) for h in range(a.shape[1]))
+        print(f"[parity] fused backward {name}: worst unit rel-L2 {worst:.3g}")
+        assert worst <= 1e-2, name
 
 
 def test_preprocess_workspace_contents():
     # workspace = [D_r = dO_r . O_r | LSE_r * log2(e)], fp32, r = (b*Hq + h)*N + i
+    # and, given a workspace with room for it, the fused alternative's fp32 dQ accumulator
+    # [rows][d] (from the next 256-byte boundary) zeroed, whatever the workspace held
     B, Hq, N, d = 2, 3, 77, 64
     host, g = make(B, Hq, Hq, N, d, seed=9960, with_do=True)
     o, lse = api.forward(g["q"], g["k"], g["v"], False, 0.125)
-    ws = torch.zeros(api.workspace_bytes(B, Hq, N), dtype=torch.uint8, device=dev())
+    ws = torch.full((api.fused_workspace_bytes(B, Hq, N, d),), 0xFF, dtype=torch.uint8, device=dev())
     dq, dk, dv = torch.empty_like(g["q"]), torch.empty_like(g["k"]), torch.empty_like(g["v"])
     api.backward_steps(g["q"], g["k"], g["v"], o, g["do"], lse, False, 0.125, dq, dk, dv, ws, steps=("pre",))
     torch.cuda.synchronize()
@@ -436,6 +475,8 @@ def test_preprocess_workspace_contents():
     assert np.abs(w[:rows] - d_ref).max() <= 1e-5 * max(1.0, np.abs(d_ref).max())
     lse2 = (lse.cpu().reshape(-1) * torch.tensor(1.4426950408889634, dtype=torch.float32)).numpy()
     assert np.array_equal(w[rows:2 * rows], lse2)
+    acc0 = ((8 * rows + 255) // 256) * 256 // 4
+    assert (w[acc0:acc0 + rows * d] == 0).all()
 
 
 def test_tiny_f32_workload():
