@@ -223,12 +223,18 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, co
     ro.init(l32, hh);
     TrOffsets<D> to;
     to.init(lane);
+    // Items run tile-major: item it is query tile it / G (dense: from the last visible
+    // tile down; block-sparse: list entry it / G) of query head it % G of the group.  The
+    // workgroups of one KV head (its key blocks, which the launch geometry runs together
+    // on one XCD) then visit the same query tiles at the same time, so that XCD's L2
+    // serves their repeated reads of each Q/dO tile (most of all with many query heads
+    // per KV head).
     auto item_q0 = [&](int it) {
-        if constexpr (SPARSE) return (int)(list[it % per_head] & kSparseTileMask) * C::BQ;
-        return (qt_start + it % per_head) * C::BQ;
+        if constexpr (SPARSE) return (int)(list[it / G] & kSparseTileMask) * C::BQ;
+        return (qt_start + per_head - 1 - it / G) * C::BQ;
     };
     auto issue_item = [&](int it) {
-        const int hq = hkv * G + it / per_head;
+        const int hq = hkv * G + it % G;
         const int q0 = item_q0(it);
         const size_t roff = (size_t)(b * p.Hq + hq) * N + q0;
         uint16_t* st = smem + (it % C::NSTAGE) * C::STAGE;
@@ -252,7 +258,7 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, co
         const float* lse2 = (const float*)(st + 2 * C::NAT);
         const float* dvec = lse2 + C::BQ;
         bool act = have && active(q0);
-        if constexpr (SPARSE) act = act && ((list[(mine < 0 ? 0 : mine) % per_head] >> wbit) & 1u);
+        if constexpr (SPARSE) act = act && ((list[(mine < 0 ? 0 : mine) / G] >> wbit) & 1u);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();                                               // A
         if (it + 1 < nitems) issue_item(it + 1);
@@ -417,9 +423,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 // The dQ tile products read dS transposed (A operand: query rows, keys along k) and
 // the workgroup's K tile transposed (B operand: d columns, keys along k), both with
 // the transposing LDS read.  Two Q/dO stages, K (two 64-key tiles) and two P/dS slots
-// fit the LDS (129 KB at d = 128).  Items run over (query head of the group, query
-// tile), the tiles from last to first, so the workgroups of neighbouring key blocks
-// visit the same query tile together and its Q/dO reads and dQ atomics meet in L2.
+// fit the LDS (129 KB at d = 128).  Items run tile-major (query tiles from last to
+// first, the group's query heads within a tile), as in the dK/dV kernel.
 // Keys at or beyond N are masked like hidden pairs (P = 0, so dS = 0).
 // ---------------------------------------------------------------------------------
 template <int D>
@@ -536,8 +541,8 @@ __device__ __forceinline__ void fused_role(const BwdParams& p, uint16_t* smem, i
     TrColOffsets<D> kco;     // K tile, d block dbq
     kco.init(lane, dbq);
 
-    auto item_q0 = [&](int it) { return (qt_start + per_head - 1 - it % per_head) * C::BQ; };
-    auto item_row = [&](int it) { return (size_t)(b * p.Hq + hkv * G + it / per_head) * N + item_q0(it); };
+    auto item_q0 = [&](int it) { return (qt_start + per_head - 1 - it / G) * C::BQ; };
+    auto item_row = [&](int it) { return (size_t)(b * p.Hq + hkv * G + it % G) * N + item_q0(it); };
     auto issue_item = [&](int it) {
         const int q0 = item_q0(it);
         const size_t roff = item_row(it);
