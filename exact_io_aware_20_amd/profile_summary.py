@@ -186,6 +186,7 @@ def _write_traffic_md(t, out, command):
 
 
 MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+MFMA_TAG = "mfma-json:"
 
 
 def gpu_agent(pmc_dir: str) -> dict:
@@ -201,21 +202,42 @@ def gpu_agent(pmc_dir: str) -> dict:
     return {"simds": 1024, "xcc": 8}
 
 
+def mean_durations(trace_dir: str) -> dict[str, float]:
+    """Mean dispatch duration (ns) per kernel from a kernel_trace.csv, or {} if none."""
+    try:
+        path = _find(trace_dir, "kernel_trace.csv")
+    except FileNotFoundError:
+        return {}
+    per = defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            per[short_name(r["Kernel_Name"])].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return {k: sum(v) / len(v) for k, v in per.items() if v}
+
+
 def mfma_busy(pmc_dir: str) -> dict:
     """Per attention kernel: the means per dispatch of SQ_VALU_MFMA_BUSY_CYCLES (summed
     over every SIMD) and GRBM_GUI_ACTIVE (GPU-busy cycles of the dispatch, which the
     profiler sums over the XCDs, each having its own counter), and the share of SIMD
-    cycles the matrix pipe was busy: busy / (active / XCDs x SIMDs)."""
+    cycles the matrix pipe was busy: busy / (active / XCDs x SIMDs).  When the run also
+    traced the kernels (--kernel-trace), the shader clock the kernel ran at follows as
+    (active / XCDs) / mean duration."""
     agent = gpu_agent(pmc_dir)
     busy = counter_means(pmc_dir, MFMA_COUNTERS[0])
     active = counter_means(pmc_dir, MFMA_COUNTERS[1])
+    dur = mean_durations(pmc_dir)
     out = {}
     for k, b in busy.items():
         if "fa_" not in k or k not in active or active[k] <= 0:
             continue
         cycles = active[k] / agent["xcc"]
-        out[short_name(k)] = {"mfma_busy": b, "gui_active": active[k], "frac": b / (cycles * agent["simds"])}
-    return {"agent": agent, "kernels": out}
+        v = {"mfma_busy": b, "gui_active": active[k], "frac": b / (cycles * agent["simds"])}
+        d = dur.get(short_name(k))
+        if d:
+            v["duration_us"] = d / 1e3
+            v["clock_mhz"] = cycles / d * 1e3
+        out[short_name(k)] = v
+    return {"agent": agent, "kernels": out, "source_digest": source_digest()}
 
 
 def _write_mfma_md(m, out, command):
@@ -228,11 +250,32 @@ def _write_mfma_md(m, out, command):
              "the profiler sums GRBM_GUI_ACTIVE over the XCDs). It counts executed MFMAs, so for dQ it "
              "includes the recomputed S and dP contractions, and it is measured against the clock the "
              f"kernel ran at, not the 2.4 GHz of the published peak. Kernel sources digest: `{source_digest()}`.",
-             "", "| kernel | SQ_VALU_MFMA_BUSY_CYCLES | GRBM_GUI_ACTIVE | frac |", "|---|---|---|---|"]
+             "`clock` = (GRBM_GUI_ACTIVE / XCDs) / mean dispatch duration of the same run (the shader clock "
+             "under this kernel's load).",
+             "", "| kernel | SQ_VALU_MFMA_BUSY_CYCLES | GRBM_GUI_ACTIVE | frac | duration (us) | clock (MHz) |",
+             "|---|---|---|---|---|---|"]
     for k, v in sorted(m["kernels"].items()):
-        lines.append(f"| {k} | {v['mfma_busy']:.4g} | {v['gui_active']:.4g} | {v['frac']:.3f} |")
+        dur = f"{v['duration_us']:.1f}" if "duration_us" in v else "-"
+        clk = f"{v['clock_mhz']:.0f}" if "clock_mhz" in v else "-"
+        lines.append(f"| {k} | {v['mfma_busy']:.4g} | {v['gui_active']:.4g} | {v['frac']:.3f} | {dur} | {clk} |")
+    lines += ["", MFMA_TAG + " " + json.dumps(m)]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
+
+
+def committed_mfma(md_path: str, kernel: str):
+    """The MFMA-busy figures (and clock) of `kernel` from a committed summary, or None
+    when the file is missing or the kernel sources changed since."""
+    if not os.path.exists(md_path):
+        return None
+    with open(md_path) as f:
+        for line in f:
+            if line.startswith(MFMA_TAG):
+                data = json.loads(line[len(MFMA_TAG):])
+                if data.get("source_digest") != source_digest():
+                    return None
+                return data["kernels"].get(kernel)
+    return None
 
 
 STATE_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY",
