@@ -125,6 +125,65 @@ __device__ __forceinline__ f32x16 qk_half(const RowAddr<D>& ra, const u32x4 (&bf
     return c;
 }
 
+// acc^T += T^T X over both query halves (16 MFMAs into the DB accumulators), in a
+// scheduling region of its own with each MFMA's transposed A fragment read three MFMAs
+// ahead (a ring of four), as qk_both does for the S-type products.
+template <int D>
+__device__ __forceinline__ void acc_both(const TrAddr<D>& ta, const u32x4 (&bf)[2][2], f32x16 (&acc)[D / 32]) {
+    constexpr int DB = D / 32;
+    constexpr int M = 2 * 2 * DB;   // (qb, h2, db)
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 a[4];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) a[m] = ta.frag(m % DB, 16 * (m / DB));
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        if (m + 3 < M) a[(m + 3) & 3] = ta.frag((m + 3) % DB, 16 * ((m + 3) / DB));
+        acc[m % DB] = mfma32x32x16(a[m & 3], bf[m / (2 * DB)][(m / DB) & 1], acc[m % DB]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // transposed reads of MFMAs 0-2
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        if (m + 3 < M) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // reads of MFMA m+3
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA m
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Both query halves at once, in a scheduling region of their own: the two accumulation
+// chains interleaved, and each k-step's two A fragments read two steps ahead of their
+// MFMAs (a ring of three steps), so that an MFMA's operands are never the youngest LDS
+// reads in flight and the wait in front of it leaves the next reads outstanding.
+template <int D>
+__device__ __forceinline__ void qk_both(const RowAddr<D>& ra, const u32x4 (&bf)[D / 16], f32x16 (&c)[2]) {
+    constexpr int K = D / 16;
+    __builtin_amdgcn_sched_barrier(0);
+    c[0] = zero16();
+    c[1] = zero16();
+    u32x4 a[3][2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        a[k][0] = lds16_a(ra.a[k]);
+        a[k][1] = lds16_a(ra.a[k] + 2 * 32 * D);
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        if (k + 2 < K) {
+            a[(k + 2) % 3][0] = lds16_a(ra.a[k + 2]);
+            a[(k + 2) % 3][1] = lds16_a(ra.a[k + 2] + 2 * 32 * D);
+        }
+        c[0] = mfma32x32x16(a[k % 3][0], bf[k], c[0]);
+        c[1] = mfma32x32x16(a[k % 3][1], bf[k], c[1]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS reads of steps 0 and 1
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        if (k + 2 < K) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // reads of step k+2
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                  // MFMAs of step k
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Set S to -inf where the query row is >= N or outside this key's band
 // key - wr <= query <= key + wl, so that 2^(S*sl2 - LSE2) is exactly 0 there.
 // Queries of register r: qrow0 + 8(r/4) + r%4.
@@ -272,8 +331,7 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, co
                 const bool mask = q0 < kw0 + 31 - wr || q0 + C::BQ > N || q0 + C::BQ - 1 > kw0 + wl;
                 {
                     const RowAddr<D> ra(ro, lds_addr(st));
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) x[qb] = qk_half<D>(ra, bfr, qb);
+                    qk_both<D>(ra, bfr, x);
                 }
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb) {
@@ -304,8 +362,7 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, co
                     }
                 {
                     const RowAddr<D> ra(ro, lds_addr(st + C::NAT));
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) x[qb] = qk_half<D>(ra, bfr, qb);
+                    qk_both<D>(ra, bfr, x);
                 }
             }
         }
@@ -321,8 +378,7 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, co
                     for (int h2 = 0; h2 < 2; ++h2) *(u32x4*)(pb + ((2 * qb + h2) * 64 + lane) * 4) = bf[qb][h2];
                 }
                 const TrAddr<D> ta(to, lds_addr(st + C::NAT));
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) acc_half<D>(ta, bf[qb], acc, qb);   // dV^T += dO^T P
+                acc_both<D>(ta, bf, acc);   // dV^T += dO^T P
             } else {
                 u32x4 bf[2][2];
 #pragma unroll
@@ -336,8 +392,7 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, co
                     pack_half(x[qb], bf[qb]);
                 }
                 const TrAddr<D> ta(to, lds_addr(st));
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) acc_half<D>(ta, bf[qb], acc, qb);   // dK^T += Q^T dS
+                acc_both<D>(ta, bf, acc);   // dK^T += Q^T dS
             }
         }
     }
