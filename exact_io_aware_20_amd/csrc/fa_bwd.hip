@@ -153,11 +153,15 @@ __device__ __forceinline__ void acc_both(const TrAddr<D>& ta, const u32x4 (&bf)[
 // Both query halves at once, in a scheduling region of their own: the two accumulation
 // chains interleaved, and each k-step's two A fragments read two steps ahead of their
 // MFMAs (a ring of three steps), so that an MFMA's operands are never the youngest LDS
-// reads in flight and the wait in front of it leaves the next reads outstanding.
-template <int D>
-__device__ __forceinline__ void qk_both(const RowAddr<D>& ra, const u32x4 (&bf)[D / 16], f32x16 (&c)[2]) {
+// reads in flight and the wait in front of it leaves the next reads outstanding.  The
+// caller's vector work `vec` (independent of these products) is placed in the same
+// region, NV instructions after each MFMA, so this wave's vector ALU runs under its own
+// matrix work.
+template <int D, int NV = 0, typename F>
+__device__ __forceinline__ void qk_both(const RowAddr<D>& ra, const u32x4 (&bf)[D / 16], f32x16 (&c)[2], F&& vec) {
     constexpr int K = D / 16;
     __builtin_amdgcn_sched_barrier(0);
+    vec();
     c[0] = zero16();
     c[1] = zero16();
     u32x4 a[3][2];
@@ -179,7 +183,43 @@ __device__ __forceinline__ void qk_both(const RowAddr<D>& ra, const u32x4 (&bf)[
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         if (k + 2 < K) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // reads of step k+2
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                  // MFMAs of step k
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA, chain 0
+        if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);     // vector work
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA, chain 1
+        if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+template <int D>
+__device__ __forceinline__ void qk_both(const RowAddr<D>& ra, const u32x4 (&bf)[D / 16], f32x16 (&c)[2]) {
+    qk_both<D, 0>(ra, bf, c, [] {});
+}
+
+// acc^T += T^T X over one query half qb (2 DB MFMAs into the DB accumulators), the
+// transposed A fragments read three MFMAs ahead (a ring of four), with the caller's
+// independent vector work `vec` placed NV instructions after each MFMA, in one
+// scheduling region.
+template <int D, int NV, typename F>
+__device__ __forceinline__ void acc_half_mixed(const TrAddr<D>& ta, const u32x4 (&bfh)[2], f32x16 (&acc)[D / 32],
+                                               int qb, F&& vec) {
+    constexpr int DB = D / 32;
+    constexpr int M = 2 * DB;   // (h2, db)
+    __builtin_amdgcn_sched_barrier(0);
+    vec();
+    u32x4 a[4];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) a[m] = ta.frag(m % DB, 32 * qb + 16 * (m / DB));
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        if (m + 3 < M) a[(m + 3) & 3] = ta.frag((m + 3) % DB, 32 * qb + 16 * ((m + 3) / DB));
+        acc[m % DB] = mfma32x32x16(a[m & 3], bfh[m / DB], acc[m % DB]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // transposed reads of MFMAs 0-2
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        if (m + 3 < M) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // reads of MFMA m+3
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA m
+        if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);     // vector work
     }
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -321,8 +361,13 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, co
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();                                               // A
         if (it + 1 < nitems) issue_item(it + 1);
+        // Each wave overlaps its own vector work with its own matrix work: the second
+        // query half's vector work runs in the scheduling region of the first half's
+        // dV or dK products (P/dV: exponentials, bf16 packing and the hand-over of P;
+        // dS/dK: dS = P (dP - D) and its packing), and dS/dK unpacks the handed-over P
+        // under its dP products.
         f32x16 x[2];                                                   // P (P/dV) or dP (dS/dK)
-        f32x16 pp[2];                                                  // dS/dK: P of its item
+        u32x4 bf[2][2];                                                // P or dS, bf16 B fragments
         // the wave whose result the other waits on issues first: P/dV while it forms
         // P, dS/dK while it forms dS and dK
         __builtin_amdgcn_s_setprio(PV ? 2 : 0);
@@ -333,67 +378,93 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, co
                     const RowAddr<D> ra(ro, lds_addr(st));
                     qk_both<D>(ra, bfr, x);
                 }
+                if (mask) {
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    if (mask) mask_half(x[qb], q0 + 32 * qb + 4 * hh, key, N, wl, wr);
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const f32x4 L = *(const f32x4*)(lse2 + 32 * qb + 8 * g + 4 * hh);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            x[qb][4 * g + i] = fast_exp2(__builtin_fmaf(x[qb][4 * g + i], sl2, -L[i]));
-                    }
+                    for (int qb = 0; qb < 2; ++qb) mask_half(x[qb], q0 + 32 * qb + 4 * hh, key, N, wl, wr);
                 }
-            } else {
-                const uint32_t* pb = pbuf + (mine & 1) * 4 * 64 * 16;
+                uint32_t* pb = pbuf + (mine & 1) * 4 * 64 * 16;
+                f32x4 L[2][4];
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        const u32x4 v = *(const u32x4*)(pb + ((2 * qb + h2) * 64 + lane) * 4);
+                    for (int g = 0; g < 4; ++g) L[qb][g] = *(const f32x4*)(lse2 + 32 * qb + 8 * g + 4 * hh);
+                // P of one half: 2^(S sl2 - LSE2), packed to bf16 and handed over
+                auto probs = [&](int qb) __attribute__((always_inline)) {
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            // inverse of pack_half: word j of fragment h2 holds registers
-                            // r and r + 1, r = 4 (2 h2 + j/2) + 2 (j%2)
-                            const int r = 4 * (2 * h2 + (j >> 1)) + 2 * (j & 1);
-                            pp[qb][r] = bf16_lo(v[j]);
-                            pp[qb][r + 1] = bf16_hi(v[j]);
-                        }
-                    }
-                {
-                    const RowAddr<D> ra(ro, lds_addr(st + C::NAT));
-                    qk_both<D>(ra, bfr, x);
-                }
-            }
-        }
-        __builtin_amdgcn_s_setprio(PV ? 0 : 2);
-        if (act) {
-            if constexpr (PV) {
-                u32x4 bf[2][2];
-                uint32_t* pb = pbuf + (mine & 1) * 4 * 64 * 16;
+                    for (int g = 0; g < 4; ++g)
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
+                        for (int i = 0; i < 4; ++i)
+                            x[qb][4 * g + i] = fast_exp2(__builtin_fmaf(x[qb][4 * g + i], sl2, -L[qb][g][i]));
                     pack_half(x[qb], bf[qb]);
+                };
+                auto hand_over = [&](int qb) __attribute__((always_inline)) {
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2) *(u32x4*)(pb + ((2 * qb + h2) * 64 + lane) * 4) = bf[qb][h2];
-                }
+                };
+                probs(0);
+                hand_over(0);
+                __builtin_amdgcn_s_setprio(0);
                 const TrAddr<D> ta(to, lds_addr(st + C::NAT));
-                acc_both<D>(ta, bf, acc);   // dV^T += dO^T P
+                // The empty asm pins the start of half 1's vector work inside the region (pure
+                // arithmetic is otherwise free to be placed before it).  Its hand-over is
+                // written after the region: the compiler cannot tell that store from the
+                // region's dO reads apart, and would order every read behind it.
+                acc_half_mixed<D, 5>(ta, bf[0], acc, 0, [&] {                 // dV^T += dO^T P, half 0
+                    asm volatile("" : "+v"(x[1]));
+                    probs(1);
+                });
+                hand_over(1);
+                acc_half_mixed<D, 0>(ta, bf[1], acc, 1, [] {});               // half 1
             } else {
-                u32x4 bf[2][2];
+                const uint32_t* pb = pbuf + (mine & 1) * 4 * 64 * 16;
+                u32x4 praw[2][2];
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
+                for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const f32x4 Dd = *(const f32x4*)(dvec + 32 * qb + 8 * g + 4 * hh);
+                    for (int h2 = 0; h2 < 2; ++h2) praw[qb][h2] = *(const u32x4*)(pb + ((2 * qb + h2) * 64 + lane) * 4);
+                f32x16 pp[2];                                              // P of its item
+                // inverse of pack_half: word j of fragment h2 holds registers r and r + 1,
+                // r = 4 (2 h2 + j/2) + 2 (j%2)
+                auto unpack = [&] {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) x[qb][4 * g + i] = pp[qb][4 * g + i] * (x[qb][4 * g + i] - Dd[i]);
-                    }
-                    pack_half(x[qb], bf[qb]);
+                    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const int r = 4 * (2 * h2 + (j >> 1)) + 2 * (j & 1);
+                                pp[qb][r] = bf16_lo(praw[qb][h2][j]);
+                                pp[qb][r + 1] = bf16_hi(praw[qb][h2][j]);
+                            }
+                };
+                {
+                    const RowAddr<D> ra(ro, lds_addr(st + C::NAT));
+                    qk_both<D, 1>(ra, bfr, x, unpack);                      // dP = dO V^T
                 }
+                f32x4 Dd[2][4];
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) Dd[qb][g] = *(const f32x4*)(dvec + 32 * qb + 8 * g + 4 * hh);
+                auto dsoft = [&](int qb) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            x[qb][4 * g + i] = pp[qb][4 * g + i] * (x[qb][4 * g + i] - Dd[qb][g][i]);
+                    pack_half(x[qb], bf[qb]);
+                };
+                __builtin_amdgcn_s_setprio(2);
+                dsoft(0);
                 const TrAddr<D> ta(to, lds_addr(st));
-                acc_both<D>(ta, bf, acc);   // dK^T += Q^T dS
+                acc_half_mixed<D, 5>(ta, bf[0], acc, 0, [&] {                 // dK^T += Q^T dS, half 0
+                    asm volatile("" : "+v"(x[1]));
+                    dsoft(1);
+                });
+                acc_half_mixed<D, 0>(ta, bf[1], acc, 1, [] {});               // half 1
             }
+        } else {
+            __builtin_amdgcn_s_setprio(PV ? 0 : 2);
         }
     }
 
