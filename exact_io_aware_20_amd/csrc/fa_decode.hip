@@ -125,10 +125,23 @@ void fa_decode_split_kernel(DecodeParams p) {
         if (PAGED) return t * kDecodeTile;
         return Nk >= kDecodeTile ? min(t * kDecodeTile, Nk - kDecodeTile) : 0;
     };
+    // The table entries of 64 consecutive pages of the sequence are held one per lane
+    // and handed out by a lane shuffle, so that finding a tile's page needs no memory
+    // round trip in front of its loads (one table read per 64 pages).
+    int pchunk = -1, pent = 0;
+    auto page_entry = [&](int pi) {
+        const int c = pi >> 6;
+        if (c != pchunk) {
+            const int e = 64 * c + lane;
+            pent = e < p.max_blocks ? p.block_table[(size_t)b * p.max_blocks + e] : -1;
+            pchunk = c;
+        }
+        return __shfl(pent, pi & 63);
+    };
     auto tile_off = [&](int t, bool& bad) -> size_t {
         if constexpr (PAGED) {
             const int key = t * kDecodeTile;
-            int pg = p.block_table[(size_t)b * p.max_blocks + key / p.page_size];
+            int pg = page_entry(key / p.page_size);
             bad = (unsigned)pg >= (unsigned)p.num_pages;
             pg = bad ? 0 : pg;
             return (((size_t)pg * p.Hkv + hkv) * p.page_size + key % p.page_size) * D;

@@ -19,7 +19,9 @@ constexpr int kDecodeTile = 64;   // keys per decode K/V tile
 // Decode: one single-wave workgroup per SIMD, four per CU on 256 CUs.  Paged calls plan
 // for their longest sequence (the only length the host knows), so with mixed lengths the
 // splits past a shorter sequence's end exit at once; planning more, shorter splits
-// (2048 to 4096), or issuing splits before sequences, measured slower.
+// (2048 to 4096), issuing splits before sequences, or balancing the splits over the
+// tokens the sequences hold (lengths read on the device, every SIMD streaming) measured
+// slower: the paged split is capped by the memory system's rate for scattered pages.
 constexpr int kDecodeTargetWgs = 1024;
 
 struct FwdParams {
