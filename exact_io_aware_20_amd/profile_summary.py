@@ -251,7 +251,9 @@ def _write_mfma_md(m, out, command):
              "includes the recomputed S and dP contractions, and it is measured against the clock the "
              f"kernel ran at, not the 2.4 GHz of the published peak. Kernel sources digest: `{source_digest()}`.",
              "`clock` = (GRBM_GUI_ACTIVE / XCDs) / mean dispatch duration of the same run (the shader clock "
-             "under this kernel's load).",
+             "under this kernel's load). Only dispatches of a millisecond or more give a usable figure: for "
+             "shorter ones the counter also covers cycles outside the traced duration, and the quotient "
+             "exceeds the 2.4 GHz maximum.",
              "", "| kernel | SQ_VALU_MFMA_BUSY_CYCLES | GRBM_GUI_ACTIVE | frac | duration (us) | clock (MHz) |",
              "|---|---|---|---|---|---|"]
     for k, v in sorted(m["kernels"].items()):
