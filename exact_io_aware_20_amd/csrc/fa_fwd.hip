@@ -318,9 +318,12 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
         ++t;
     }
-    for (; t < ntiles; t += 2) {
+    // one general step per iteration, the scores handed over by copy: unrolled by two
+    // (swapping the two score sets) the loop spilled 8 registers to scratch
+    for (; t < ntiles; ++t) {
         step(t, sa, sb);
-        if (t + 1 < ntiles) step(t + 1, sb, sa);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sa[kb] = sb[kb];
     }
 
     // ---- epilogue: O = O^T / l (bf16, round to nearest even), LSE in natural log
