@@ -607,6 +607,12 @@ void fa_fwd_sparse_kernel(FwdParams p) {
     const int q = qw0 + l32;
     const int nb = (N + kSparseBlock - 1) / kSparseBlock;
     const int qb0 = q0 / kSparseBlock;
+    // Q fragments first, so that their loads are in flight with the layout reads of
+    // the list build (B operand of S^T = K Q^T, lane: query)
+    u32x4 qf[C::DC];
+#pragma unroll
+    for (int c = 0; c < C::DC; ++c)
+        qf[c] = q < N ? ld_global16(Qh + (size_t)q * D + 16 * c + 8 * hh) : zero_u4();
     if (wave == 0) {
         const int u_end = p.causal ? min(nb, qb0 + C::BR / kSparseBlock) : nb;   // later key tiles are masked
         const int n = compact_tiles(list, 0, u_end, lane, [&](int u) -> uint32_t {
@@ -625,10 +631,6 @@ void fa_fwd_sparse_kernel(FwdParams p) {
     const int cnt = list_n;
     const int wbit = 20 + wave / (kSparseBlock / 32);   // this wave's block within the workgroup
 
-    u32x4 qf[C::DC];
-#pragma unroll
-    for (int c = 0; c < C::DC; ++c)
-        qf[c] = q < N ? ld_global16(Qh + (size_t)q * D + 16 * c + 8 * hh) : zero_u4();
     f32x16 o[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) o[db] = zero16();
