@@ -357,7 +357,7 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, co
         const float* lse2 = (const float*)(st + 2 * C::NAT);
         const float* dvec = lse2 + C::BQ;
         bool act = have && active(q0);
-        if constexpr (SPARSE) act = act && ((list[(mine < 0 ? 0 : mine) / G] >> wbit) & 1u);
+        if constexpr (SPARSE) act = act && ((list[have ? mine / G : 0] >> wbit) & 1u);   // no read past the list
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();                                               // A
         if (it + 1 < nitems) issue_item(it + 1);
@@ -880,6 +880,49 @@ struct DqCfg {
     static_assert(BR == kDqRows, "launch plan and kernel disagree on the row tile");
 };
 
+// S^T = K Q^T and dP^T = V dO^T of one key tile in a scheduling region of their own:
+// the four accumulation chains (S and dP of the two 32-key blocks) taken in turn, chunk
+// by chunk, each A fragment read two MFMAs ahead (a ring of three), so that a read is
+// never waited for by the MFMA right behind it.  Every register accumulates its chunks
+// in the same order as a plain loop over them.
+template <int D>
+__device__ __forceinline__ void dq_scores(const uint16_t* st, const u32x4 (&qf)[D / 16], const u32x4 (&gf)[D / 16],
+                                          f32x16 (&s)[2], f32x16 (&dp)[2], int l32, int hh) {
+    using C = DqCfg<D>;
+    using KS = SwzTile<D, 1>;
+    using VS = SwzTile<D, 0>;
+    constexpr int M = 4 * C::DC;   // m: chunk m/4, r = m%4: S block 0, dP block 0, S block 1, dP block 1
+    auto frag = [&](int m) __attribute__((always_inline)) -> u32x4 {
+        const int c = m >> 2, r = m & 3, kb = r >> 1;
+        if ((r & 1) == 0) return lds16(st + KS::at(32 * kb + l32, 2 * c + hh));
+        return lds16(st + C::KT + VS::at(32 * kb + l32, 2 * c + hh));
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    s[0] = zero16();
+    s[1] = zero16();
+    dp[0] = zero16();
+    dp[1] = zero16();
+    u32x4 a[3];
+    a[0] = frag(0);
+    a[1] = frag(1);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        if (m + 2 < M) a[(m + 2) % 3] = frag(m + 2);
+        const int c = m >> 2, r = m & 3, kb = r >> 1;
+        if ((r & 1) == 0)
+            s[kb] = mfma32x32x16(a[m % 3], qf[c], s[kb]);
+        else
+            dp[kb] = mfma32x32x16(a[m % 3], gf[c], dp[kb]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // reads of MFMAs 0 and 1
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        if (m + 2 < M) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // read of MFMA m+2
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA m
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // dQ kernel: per key/value tile, S^T = K Q^T and dP^T = V dO^T (lane: query),
 // dS^T = P^T (dP^T - D) rounded to bf16, dQ^T += K^T dS^T with K^T read transposed
 // from the natural K tile.  K/V tiles are double-buffered with one barrier each.
@@ -990,14 +1033,8 @@ void fa_bwd_dq_kernel(BwdParams p) {
             // keeps the matrix pipe fed while its SIMD partner runs dS (measured
             // 0.4-0.5 % faster than equal priorities)
             __builtin_amdgcn_s_setprio(3);
-            f32x16 s[2] = {zero16(), zero16()}, dp[2] = {zero16(), zero16()};
-#pragma unroll
-            for (int c = 0; c < C::DC; ++c)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    s[kb] = mfma32x32x16(lds16(st + KS::at(32 * kb + l32, 2 * c + hh)), qf[c], s[kb]);
-                    dp[kb] = mfma32x32x16(lds16(st + C::KT + VS::at(32 * kb + l32, 2 * c + hh)), gf[c], dp[kb]);
-                }
+            f32x16 s[2], dp[2];
+            dq_scores<D>(st, qf, gf, s, dp, l32, hh);
             if (k0 + C::BC - 1 > qw0 + wr || k0 + C::BC > N || k0 < wq_last - wl) {
                 const int lo = q - wl, hi = min(q + wr, N - 1);
 #pragma unroll
