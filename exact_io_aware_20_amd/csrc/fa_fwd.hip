@@ -215,7 +215,7 @@ void fa_fwd_bf16_kernel(FwdParams p) {
             const TrAddr<D> va(voff, lds_addr(buf));
             fwd_pv_a<D>(va, pf, o);
         } else {
-            fwd_pv<D>(buf, pf, o, lane);
+            fwd_pv_ring<D>(buf, pf, o, lane);
         }
     };
 

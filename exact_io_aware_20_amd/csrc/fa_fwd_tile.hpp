@@ -117,4 +117,35 @@ __device__ __forceinline__ void fwd_pv(const uint16_t* Vt, const u32x4 (&pf)[2][
                 o[db] = mfma32x32x16(tr_frag<D>(Vt, db, 32 * kb + 16 * h2, lane), pf[kb][h2], o[db]);
 }
 
+// fwd_pv in a scheduling region of its own: the transposed V fragments read three
+// MFMAs ahead (a ring of four), so that an MFMA's operand is never the youngest read in
+// flight.  Same accumulation order as fwd_pv.
+template <int D>
+__device__ __forceinline__ void fwd_pv_ring(const uint16_t* Vt, const u32x4 (&pf)[2][2], f32x16 (&o)[D / 32],
+                                            int lane) {
+    constexpr int DB = D / 32;
+    constexpr int M = 4 * DB;   // m: column block m % DB of (kb, h2) = (m / DB) / 2, (m / DB) % 2
+    auto frag = [&](int m) __attribute__((always_inline)) {
+        const int kh = m / DB;
+        return tr_frag<D>(Vt, m % DB, 32 * (kh >> 1) + 16 * (kh & 1), lane);
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 a[4];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) a[m] = frag(m);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        if (m + 3 < M) a[(m + 3) & 3] = frag(m + 3);
+        const int kh = m / DB;
+        o[m % DB] = mfma32x32x16(a[m & 3], pf[kh >> 1][kh & 1], o[m % DB]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // reads of MFMAs 0-2
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        if (m + 3 < M) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // reads of MFMA m+3
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA m
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 }  // namespace fa
