@@ -99,6 +99,35 @@ __device__ __forceinline__ void fwd_pv_a(const TrAddr<D>& va, const u32x4 (&pf)[
             for (int db = 0; db < D / 32; ++db) o[db] = mfma32x32x16(va.frag(db, 32 * kb + 16 * h2), pf[kb][h2], o[db]);
 }
 
+// fwd_pv_a in a scheduling region of its own, the transposed V fragments read three
+// MFMAs ahead (a ring of four); same accumulation order.
+template <int D>
+__device__ __forceinline__ void fwd_pv_a_ring(const TrAddr<D>& va, const u32x4 (&pf)[2][2], f32x16 (&o)[D / 32]) {
+    constexpr int DB = D / 32;
+    constexpr int M = 4 * DB;   // m: column block m % DB of (kb, h2) = (m / DB) / 2, (m / DB) % 2
+    auto frag = [&](int m) __attribute__((always_inline)) {
+        const int kh = m / DB;
+        return va.frag(m % DB, 32 * (kh >> 1) + 16 * (kh & 1));
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 a[4];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) a[m] = frag(m);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        if (m + 3 < M) a[(m + 3) & 3] = frag(m + 3);
+        const int kh = m / DB;
+        o[m % DB] = mfma32x32x16(a[m & 3], pf[kh >> 1][kh & 1], o[m % DB]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // reads of MFMAs 0-2
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        if (m + 3 < M) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // reads of MFMA m+3
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA m
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Epilogue store of one query row (row index `row` of [B*Hq*N]): the lane's O^T
 // registers times inv = 1/l, rounded to bf16 (round to nearest even).  With the
 // validation pointer p.o32 set, the same fp32 products are stored unrounded instead.
@@ -435,7 +464,7 @@ void fa_fwd_persist_kernel(FwdParams p) {
     };
     auto pv_of = [&](const uint16_t* buf, const u32x4 (&pf)[2][2]) __attribute__((always_inline)) {
         const TrAddr<D> va(voff, lds_addr(buf));
-        fwd_pv_a<D>(va, pf, o);
+        fwd_pv_a_ring<D>(va, pf, o);
     };
     // an item's Q fragments, first two K tiles and first V tile (buffer parity ph)
     auto prefetch = [&](const Geom& g, int ph) __attribute__((always_inline)) {
