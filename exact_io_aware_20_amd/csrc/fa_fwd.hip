@@ -692,20 +692,20 @@ void fa_fwd_sparse_kernel(FwdParams p) {
         if (1 < cnt) issue_k(1, kbuf + KB);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (sees(0)) fwd_scores<D>(kbuf, qf, sa, l32, hh);
+        if (sees(0)) fwd_scores_ring<D>(kbuf, qf, sa, l32, hh);
         __syncthreads();
     }
     auto step = [&](int e, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
         if (e + 2 < cnt) issue_k(e + 2, kbuf + (e & 1) * KB);
         if (e + 1 < cnt) issue_v(e + 1, vbuf + ((e + 1) & 1) * VB);
-        if (e + 1 < cnt && sees(e + 1)) fwd_scores<D>(kbuf + ((e + 1) & 1) * KB, qf, nxt, l32, hh);
+        if (e + 1 < cnt && sees(e + 1)) fwd_scores_ring<D>(kbuf + ((e + 1) & 1) * KB, qf, nxt, l32, hh);
         if (sees(e)) {
             const int k0 = tile(e) * C::BC;
             if (k0 + C::BC - 1 > qw0 + wr || k0 + C::BC > N) fwd_mask<false>(cur, k0, 0, min(q + wr, N - 1), hh);
             fwd_rescale<D>(cur, o, m_ref, l_part, sl2);
             u32x4 pf[2][2];
             fwd_probs(cur, m_ref, sl2, pf, l_part);
-            fwd_pv<D>(vbuf + (e & 1) * VB, pf, o, lane);
+            fwd_pv_ring<D>(vbuf + (e & 1) * VB, pf, o, lane);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();

@@ -39,6 +39,35 @@ __device__ __forceinline__ void fwd_scores(const uint16_t* Ks, const u32x4 (&qf)
     }
 }
 
+// fwd_scores in a scheduling region of its own: the two 32-key chains taken in turn,
+// one K fragment per MFMA read two MFMAs ahead (a ring of three); same accumulation
+// order as fwd_scores.
+template <int D>
+__device__ __forceinline__ void fwd_scores_ring(const uint16_t* Ks, const u32x4 (&qf)[D / 16], f32x16 (&s)[2],
+                                                int l32, int hh) {
+    using KT = SwzTile<D, 0>;
+    constexpr int M = D / 8;   // m: chunk m / 2 of key block m % 2
+    auto frag = [&](int m) __attribute__((always_inline)) { return lds16(Ks + KT::at(32 * (m & 1) + l32, 2 * (m >> 1) + hh)); };
+    __builtin_amdgcn_sched_barrier(0);
+    s[0] = zero16();
+    s[1] = zero16();
+    u32x4 a[3];
+    a[0] = frag(0);
+    a[1] = frag(1);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        if (m + 2 < M) a[(m + 2) % 3] = frag(m + 2);
+        s[m & 1] = mfma32x32x16(a[m % 3], qf[m >> 1], s[m & 1]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // reads of MFMAs 0 and 1
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        if (m + 2 < M) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // read of MFMA m+2
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA m
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Max over the wave's lane pair (l, l^32) that share a query column.
 __device__ __forceinline__ float pair_max(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
