@@ -29,10 +29,12 @@
  *   - Hq must be a multiple of Hkv; query head hq reads KV head hq / (Hq/Hkv)
  *     (contiguous groups).  d must be 64 or 128.  B, Hq, Hkv, N >= 1.
  *   - scale must be finite and >= 0.  causal must be 0 or 1.
- *   - The caller allocates and frees all memory.  The library allocates nothing,
- *     keeps no mutable global state and never synchronises: work is enqueued on
- *     `stream` (0 = the null stream) and results are valid after the caller
- *     synchronises that stream.  Outputs must not overlap inputs or each other.
+ *   - The caller allocates and frees all memory.  The library allocates nothing and
+ *     never synchronises: work is enqueued on `stream` (0 = the null stream) and
+ *     results are valid after the caller synchronises that stream.  Its only mutable
+ *     global state is the static scratch array of fa_backward_noalloc and that array's
+ *     per-device address, looked up once under a lock.  Outputs must not overlap
+ *     inputs or each other.
  *   - Arguments are validated on the host before anything is launched; on error
  *     nothing is launched and no output is touched.  FA_ERR_LAUNCH reports a
  *     launch failure seen by hipGetLastError; faults inside a kernel surface at
