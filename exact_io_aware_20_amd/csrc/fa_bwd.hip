@@ -277,17 +277,14 @@ __device__ __forceinline__ void acc_half(const TrAddr<D>& ta, const u32x4 (&bf)[
 // from LDS, dP, dS and the dK MFMAs of item it-1, so one wave of a SIMD pair runs
 // exponentials or dS while the other runs matrix work.
 template <int D, bool PV, bool SPARSE>
-__device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, const uint32_t* list, int list_n,
-                                          int wave, int lane) {
+__device__ __forceinline__ void dkdv_tile(const BwdParams& p, uint16_t* smem, const uint32_t* list, int list_n,
+                                          int wave, int lane, int head_kv, int kt, bool ascending) {
     using C = DkdvCfg<D>;
     const int l32 = lane & 31;
     const int hh = lane >> 5;
     const int N = p.N;
     const int G = p.Hq / p.Hkv;
 
-    const int ntile_k = (N + C::BK - 1) / C::BK;
-    int head_kv, kt;
-    map_block(blockIdx.x, gridDim.x, ntile_k, p.B * p.Hkv, false, head_kv, kt, 4);
     const int b = head_kv / p.Hkv;
     const int hkv = head_kv % p.Hkv;
     const int k0 = kt * C::BK;
@@ -323,14 +320,15 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, co
     TrOffsets<D> to;
     to.init(lane);
     // Items run tile-major: item it is query tile it / G (dense: from the last visible
-    // tile down; block-sparse: list entry it / G) of query head it % G of the group.  The
+    // tile down, or for the second tile of a pair from the first visible tile up;
+    // block-sparse: list entry it / G) of query head it % G of the group.  The
     // workgroups of one KV head (its key blocks, which the launch geometry runs together
     // on one XCD) then visit the same query tiles at the same time, so that XCD's L2
     // serves their repeated reads of each Q/dO tile (most of all with many query heads
     // per KV head).
     auto item_q0 = [&](int it) {
         if constexpr (SPARSE) return (int)(list[it / G] & kSparseTileMask) * C::BQ;
-        return (qt_start + per_head - 1 - it / G) * C::BQ;
+        return (ascending ? qt_start + it / G : qt_start + per_head - 1 - it / G) * C::BQ;
     };
     auto issue_item = [&](int it) {
         const int hq = hkv * G + it % G;
@@ -479,6 +477,31 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, co
                 *(u32x2*)(dst + 32 * db + 8 * g + 4 * hh) =
                     u32x2{pack_bf16(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc),
                           pack_bf16(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc)};
+    }
+}
+
+// A workgroup's key tiles.  Causal without a window: a pair, tile j walked from its
+// last visible query tile down, then tile ntile_k - 1 - j walked from its first visible
+// query tile up.  Every pair then holds the same number of items, so the workgroups end
+// together, and all workgroups of a KV head read the same query tile at the same time in
+// both halves (the first halves all start at the last tile; a second half starts where
+// its first ended, at a time that puts it on the same tile as every other second half).
+// Full attention, a window or a block-sparse layout: one tile, walked down; there the
+// tiles' lengths already match (up to the window's ends) and pairing only halves the grid.
+template <int D, bool PV, bool SPARSE>
+__device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, const uint32_t* list, int list_n,
+                                          int wave, int lane) {
+    using C = DkdvCfg<D>;
+    const int ntile_k = (p.N + C::BK - 1) / C::BK;
+    const bool paired = !SPARSE && p.causal && p.window < 0;
+    int head_kv, kt;
+    map_block(blockIdx.x, gridDim.x, paired ? (ntile_k + 1) / 2 : ntile_k, p.B * p.Hkv, false, head_kv, kt, 4);
+    dkdv_tile<D, PV, SPARSE>(p, smem, list, list_n, wave, lane, head_kv, kt, false);
+    const int kt2 = ntile_k - 1 - kt;
+    if (paired && kt2 != kt) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();   // every wave done with the first tile's LDS stages and P slots
+        dkdv_tile<D, PV, SPARSE>(p, smem, list, list_n, wave, lane, head_kv, kt2, true);
     }
 }
 
@@ -1138,7 +1161,10 @@ static hipError_t launch_pre(const BwdParams& p, hipStream_t stream) {
 
 template <int D>
 static hipError_t launch_dkdv(const BwdParams& p, hipStream_t stream) {
-    const unsigned blocks = (unsigned)((long long)p.B * p.Hkv * ((p.N + DkdvCfg<D>::BK - 1) / DkdvCfg<D>::BK));
+    // one workgroup per pair of key tiles (causal, no window) or per key tile
+    const long long ntk = (p.N + DkdvCfg<D>::BK - 1) / DkdvCfg<D>::BK;
+    const bool paired = !p.block_mask && p.causal && p.window < 0;
+    const unsigned blocks = (unsigned)((long long)p.B * p.Hkv * (paired ? (ntk + 1) / 2 : ntk));
     if (p.block_mask)
         hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, true>), dim3(blocks), dim3(DkdvCfg<D>::THREADS), 0, stream, p);
     else
