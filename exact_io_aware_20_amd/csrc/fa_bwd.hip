@@ -495,7 +495,10 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, co
     const int ntile_k = (p.N + C::BK - 1) / C::BK;
     const bool paired = !SPARSE && p.causal && p.window < 0;
     int head_kv, kt;
-    map_block(blockIdx.x, gridDim.x, paired ? (ntile_k + 1) / 2 : ntile_k, p.B * p.Hkv, false, head_kv, kt, 4);
+    // paired workgroups all hold the same work, so the pairs of one head, side by side on
+    // one XCD, stream that head's Q/dO tiles through its L2 together, once
+    map_block(blockIdx.x, gridDim.x, paired ? (ntile_k + 1) / 2 : ntile_k, p.B * p.Hkv, false, head_kv, kt,
+              paired ? 1 : 4);
     dkdv_tile<D, PV, SPARSE>(p, smem, list, list_n, wave, lane, head_kv, kt, false);
     const int kt2 = ntile_k - 1 - kt;
     if (paired && kt2 != kt) {
