@@ -44,6 +44,17 @@ def build_library(verbose: bool = False) -> Path:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # A kernel template whose host-side launch stub was not emitted still links into a
+    # shared library and only fails when it is loaded: refuse such a build here.
+    try:
+        nm = subprocess.run(["nm", "-D", "--undefined-only", str(tmp)], capture_output=True, text=True)
+    except FileNotFoundError:
+        nm = None
+    if nm is not None and nm.returncode == 0:
+        missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "__device_stub__" in ln]
+        if missing:
+            tmp.unlink()
+            raise RuntimeError("kernel launch stubs left undefined: " + ", ".join(missing))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

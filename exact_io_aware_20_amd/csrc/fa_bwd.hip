@@ -339,8 +339,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, uint16_t* smem, co
         dma.issue((const uint16_t*)p.dO + roff * D, N - q0, st + C::NAT, wave);
         // LSE2 (wave 0) and D (wave 1): 4 bytes per lane; rows >= N read row N-1
         if (wave < 2) {
-            const float* src = (wave == 0 ? p.lse2 : p.dsum) + roff + min(lane, N - 1 - q0);
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)(st + 2 * C::NAT + wave * 2 * C::BQ), 4, 0, 0);
+            dma_row_values((wave == 0 ? p.lse2 : p.dsum) + roff, N - q0, st + 2 * C::NAT + wave * 2 * C::BQ, lane);
         }
     };
     // keys of this wave visible to some row of the item's tile
@@ -703,8 +702,7 @@ __device__ __forceinline__ void fused_role(const BwdParams& p, uint16_t* smem, i
         dma.issue((const uint16_t*)p.dO + roff * D, N - q0, st + C::NAT, wave);
         // LSE2 (wave 0) and D (wave 1): 4 bytes per lane; rows >= N read row N-1
         if (wave < 2) {
-            const float* src = (wave == 0 ? p.lse2 : p.dsum) + roff + min(lane, N - 1 - q0);
-            __builtin_amdgcn_global_load_lds(src, (lds_void*)(st + 2 * C::NAT + wave * 2 * C::BQ), 4, 0, 0);
+            dma_row_values((wave == 0 ? p.lse2 : p.dsum) + roff, N - q0, st + 2 * C::NAT + wave * 2 * C::BQ, lane);
         }
     };
     auto active = [&](int q0) { return kw0 < N && q0 + C::BQ - 1 >= kw0 - wr && q0 <= kw0 + 31 + wl; };

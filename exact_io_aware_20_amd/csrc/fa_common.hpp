@@ -92,7 +92,7 @@ __device__ __forceinline__ void map_block(int bid, int nblk, int ntile, int nhea
 
 // ---------------------------------------------------------------------------------
 // Swizzled natural tile [64][D] in LDS, filled by direct global->LDS loads
-// (global_load_lds_dwordx4: lane L of a wave writes 16 bytes at base + 16*L).
+// (buffer_load_dwordx4 ... lds: lane L of a wave writes 16 bytes at base + 16*L).
 // Row r's 16-byte chunk j lives at slot j ^ swz(r), with no padding.
 //
 // Two read patterns touch these tiles (bank = 4-byte word index mod 64):
@@ -127,13 +127,48 @@ struct SwzTile {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Direct global->LDS loads go through buffer resources (buffer_load ... lds), not the
+// global_load_lds form.  The compiler's wait insertion counts the global form against
+// both the vector-memory and the LDS counters, and while one is in flight it turns every
+// LDS wait into lgkmcnt(0).  Every loop that prefetches its next tile would then wait for
+// all its outstanding fragment reads at each MFMA, not just the oldest.  With the buffer
+// form those waits stay exact.  The builtin is called only from the two plain
+// functions below: written inside a function template, a kernel template reaching it
+// could lose its host-side launch stub without a diagnostic.
+//
+// Buffer resource over `bytes` bytes from `base` (raw, unformatted dword access; a read
+// past the end returns zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// One direct load per lane of 16 (4) bytes at byte offset voff of r into LDS at dst +
+// 16 (4) x lane; dst is wave-uniform.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, voff, 0, 0, 0);
+}
+// The global form: 16 bytes per lane from the lane's own address.
+__device__ __forceinline__ void dma16_global(const void* src, void* dst) {
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
+
+// Direct load of one 4-byte value per lane: lane l reads element min(l, nvalid - 1) of
+// `src` into LDS at dst + 4 l.
+__device__ __forceinline__ void dma_row_values(const float* src, int nvalid, void* dst, int lane) {
+    dma4(tile_rsrc(src, nvalid * 4), (uint32_t)min(lane, nvalid - 1) * 4, dst);
+}
+
 // Direct loads of one 64-row tile: wave-instruction i (of WAVE_LOADS, spread over
 // NWAVES waves) covers LDS chunk positions [64 i, 64 i + 64).  A wave's chunk
 // positions do not change from tile to tile, so the per-lane source offsets are
 // computed once and a full tile costs one load per chunk from a uniform base plus
 // a 32-bit lane offset; only a ragged last tile (wave-uniform branch) clamps its
-// rows.  `wave` must be below NWAVES.
-template <int D, int MODE, int NWAVES>
+// rows.  `wave` must be below NWAVES.  BUF selects the buffer form (above) or the
+// global_load_lds form.
+template <int D, int MODE, int NWAVES, bool BUF = true>
 struct TileDma {
     using S = SwzTile<D, MODE>;
     static constexpr int PER = (S::WAVE_LOADS + NWAVES - 1) / NWAVES;
@@ -148,21 +183,28 @@ struct TileDma {
     }
     // all 64 rows of src are in bounds
     __device__ __forceinline__ void issue_full(const uint16_t* src, uint16_t* lds_tile, int wave) const {
-        const char* base = (const char*)src;
+        if constexpr (BUF) {
+            const __amdgpu_buffer_rsrc_t r = tile_rsrc(src, 64 * D * 2);
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int i = wave + k * NWAVES;
-            if (S::WAVE_LOADS % NWAVES == 0 || i < S::WAVE_LOADS)
-                __builtin_amdgcn_global_load_lds((const uint16_t*)(base + off[k]),
-                                                 (lds_void*)(lds_tile + i * 64 * 8), 16, 0, 0);
+            for (int k = 0; k < PER; ++k) {
+                const int i = wave + k * NWAVES;
+                if (S::WAVE_LOADS % NWAVES == 0 || i < S::WAVE_LOADS) dma16(r, off[k], lds_tile + i * 64 * 8);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int i = wave + k * NWAVES;
+                if (S::WAVE_LOADS % NWAVES == 0 || i < S::WAVE_LOADS)
+                    dma16_global((const char*)src + off[k], lds_tile + i * 64 * 8);
+            }
         }
     }
     // rows at or past `nvalid` are read from row nvalid-1 (in bounds, never used)
     __device__ __forceinline__ void issue(const uint16_t* src, int nvalid, uint16_t* lds_tile, int wave) const {
-        const char* base = (const char*)src;
         if (nvalid >= 64) {
             issue_full(src, lds_tile, wave);
         } else {
+            const __amdgpu_buffer_rsrc_t r = tile_rsrc(src, nvalid * D * 2);
 #pragma unroll
             for (int k = 0; k < PER; ++k) {
                 const int i = wave + k * NWAVES;
@@ -170,8 +212,11 @@ struct TileDma {
                     const uint32_t row = off[k] / (2 * D);
                     const uint32_t last = (uint32_t)(nvalid - 1);
                     const uint32_t rr = row < last ? row : last;
-                    __builtin_amdgcn_global_load_lds((const uint16_t*)(base + (off[k] - (row - rr) * (2 * D))),
-                                                     (lds_void*)(lds_tile + i * 64 * 8), 16, 0, 0);
+                    const uint32_t voff = off[k] - (row - rr) * (2 * D);
+                    if constexpr (BUF)
+                        dma16(r, voff, lds_tile + i * 64 * 8);
+                    else
+                        dma16_global((const char*)src + voff, lds_tile + i * 64 * 8);
                 }
             }
         }

@@ -56,7 +56,7 @@ template <int D, bool PAGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_decode_split_kernel(DecodeParams p) {
     using S = SwzTile<D, 1>;
-    using Dma = TileDma<D, 1, 1>;
+    using Dma = TileDma<D, 1, 1, false>;   // global form: 8 % faster than the buffer form here (paged)
     constexpr int T = S::ELEMS;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T];
     uint16_t* kbuf = smem;
