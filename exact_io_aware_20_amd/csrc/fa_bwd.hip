@@ -164,25 +164,28 @@ __device__ __forceinline__ void qk_both(const RowAddr<D>& ra, const u32x4 (&bf)[
     vec();
     c[0] = zero16();
     c[1] = zero16();
-    u32x4 a[3][2];
+    u32x4 a[4][2];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < 3; ++k) {
         a[k][0] = lds16_a(ra.a[k]);
         a[k][1] = lds16_a(ra.a[k] + 2 * 32 * D);
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        if (k + 2 < K) {
-            a[(k + 2) % 3][0] = lds16_a(ra.a[k + 2]);
-            a[(k + 2) % 3][1] = lds16_a(ra.a[k + 2] + 2 * 32 * D);
+        if (k + 3 < K) {
+            a[(k + 3) & 3][0] = lds16_a(ra.a[k + 3]);
+            a[(k + 3) & 3][1] = lds16_a(ra.a[k + 3] + 2 * 32 * D);
         }
-        c[0] = mfma32x32x16(a[k % 3][0], bf[k], c[0]);
-        c[1] = mfma32x32x16(a[k % 3][1], bf[k], c[1]);
+        c[0] = mfma32x32x16(a[k & 3][0], bf[k], c[0]);
+        c[1] = mfma32x32x16(a[k & 3][1], bf[k], c[1]);
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS reads of steps 0 and 1
+    // both chains end inside the region (a product used only later is otherwise sunk
+    // past its closing fence)
+    asm volatile("" : "+v"(c[0]), "+v"(c[1]));
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // DS reads of steps 0-2
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        if (k + 2 < K) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // reads of step k+2
+        if (k + 3 < K) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // reads of step k+3
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA, chain 0
         if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);     // vector work
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA, chain 1
@@ -361,8 +364,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, uint16_t* smem, co
         // Each wave overlaps its own vector work with its own matrix work: the second
         // query half's vector work runs in the scheduling region of the first half's
         // dV or dK products (P/dV: exponentials, bf16 packing and the hand-over of P;
-        // dS/dK: dS = P (dP - D) and its packing), and dS/dK unpacks the handed-over P
-        // under its dP products.
+        // dS/dK: unpacking the handed-over P, dS = P (dP - D) and its packing).
         f32x16 x[2];                                                   // P (P/dV) or dP (dS/dK)
         u32x4 bf[2][2];                                                // P or dS, bf16 B fragments
         // the wave whose result the other waits on issues first: P/dV while it forms
@@ -419,36 +421,27 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, uint16_t* smem, co
                 for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2) praw[qb][h2] = *(const u32x4*)(pb + ((2 * qb + h2) * 64 + lane) * 4);
-                f32x16 pp[2];                                              // P of its item
-                // inverse of pack_half: word j of fragment h2 holds registers r and r + 1,
-                // r = 4 (2 h2 + j/2) + 2 (j%2)
-                auto unpack = [&] {
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-                        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                const int r = 4 * (2 * h2 + (j >> 1)) + 2 * (j & 1);
-                                pp[qb][r] = bf16_lo(praw[qb][h2][j]);
-                                pp[qb][r + 1] = bf16_hi(praw[qb][h2][j]);
-                            }
-                };
                 {
                     const RowAddr<D> ra(ro, lds_addr(st + C::NAT));
-                    qk_both<D, 1>(ra, bfr, x, unpack);                      // dP = dO V^T
+                    qk_both<D>(ra, bfr, x);                                 // dP = dO V^T
                 }
                 f32x4 Dd[2][4];
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) Dd[qb][g] = *(const f32x4*)(dvec + 32 * qb + 8 * g + 4 * hh);
+                // dS = P (dP - D), P unpacked from the hand-over as it is used: register
+                // 4g+i of a half is the low (i even) or high bf16 of word 2(g%2) + i/2 of
+                // fragment g/2 (the inverse of pack_half)
                 auto dsoft = [&](int qb) __attribute__((always_inline)) {
 #pragma unroll
                     for (int g = 0; g < 4; ++g)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            x[qb][4 * g + i] = pp[qb][4 * g + i] * (x[qb][4 * g + i] - Dd[qb][g][i]);
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t w = praw[qb][g >> 1][2 * (g & 1) + (i >> 1)];
+                            const float pv = (i & 1) ? bf16_hi(w) : bf16_lo(w);
+                            x[qb][4 * g + i] = pv * (x[qb][4 * g + i] - Dd[qb][g][i]);
+                        }
                     pack_half(x[qb], bf[qb]);
                 };
                 __builtin_amdgcn_s_setprio(2);

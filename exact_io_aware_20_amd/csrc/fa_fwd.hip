@@ -280,18 +280,19 @@ void fa_fwd_bf16_kernel(FwdParams p) {
         __builtin_amdgcn_s_setprio(3);
         scores_of(kbuf + ((t + 1) & 1) * KB, nxt);
         fwd_probs(cur, m_ref, sl2, pf, l_part);
-        // Interleave the two in one instruction stream: four K-fragment reads ahead,
+        // Interleave the two in one instruction stream: six K-fragment reads ahead,
         // then per score MFMA (independent of tile t's softmax) six of its vector
         // instructions and the next fragment read, so the vector work issues while
         // the matrix pipe is busy (≈ 3 % faster than the two blocks in sequence; six
-        // per MFMA measured 0.3-1.4 % faster than four on the long-context forward,
-        // three and eight slower).
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS reads
+        // vector instructions per MFMA measured 0.3-1.4 % faster than four on the
+        // long-context forward, three and eight slower; six reads ahead 1-1.5 %
+        // faster than four, two no better).
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // DS reads
 #pragma unroll
         for (int i = 0; i < D / 8; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
-            if (i < D / 8 - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (i < D / 8 - 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(0);
@@ -512,7 +513,7 @@ void fa_fwd_persist_kernel(FwdParams p) {
             for (int i = 0; i < D / 8; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-                if (i < D / 8 - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (i < D / 8 - 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
             pv_of(vbuf + ((t + ph) & 1) * VB, pf);
