@@ -151,51 +151,43 @@ __device__ __forceinline__ void acc_both(const TrAddr<D>& ta, const u32x4 (&bf)[
 }
 
 // Both query halves at once, in a scheduling region of their own: the two accumulation
-// chains interleaved, and each k-step's two A fragments read two steps ahead of their
-// MFMAs (a ring of three steps), so that an MFMA's operands are never the youngest LDS
-// reads in flight and the wait in front of it leaves the next reads outstanding.  The
-// caller's vector work `vec` (independent of these products) is placed in the same
-// region, NV instructions after each MFMA, so this wave's vector ALU runs under its own
-// matrix work.
-template <int D, int NV = 0, typename F>
-__device__ __forceinline__ void qk_both(const RowAddr<D>& ra, const u32x4 (&bf)[D / 16], f32x16 (&c)[2], F&& vec) {
+// chains interleaved, and each k-step's two A fragments read AHEAD steps ahead of their
+// MFMAs (a ring of AHEAD + 1 steps), so that an MFMA's operands are never the youngest
+// LDS reads in flight and the wait in front of it leaves the next reads outstanding.
+// The dense dK/dV reads three steps ahead; the block-sparse one measured faster at two.
+template <int D, int AHEAD = 2>
+__device__ __forceinline__ void qk_both(const RowAddr<D>& ra, const u32x4 (&bf)[D / 16], f32x16 (&c)[2]) {
     constexpr int K = D / 16;
+    constexpr int R = AHEAD + 1;
     __builtin_amdgcn_sched_barrier(0);
-    vec();
     c[0] = zero16();
     c[1] = zero16();
-    u32x4 a[4][2];
+    u32x4 a[R][2];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
+    for (int k = 0; k < AHEAD; ++k) {
         a[k][0] = lds16_a(ra.a[k]);
         a[k][1] = lds16_a(ra.a[k] + 2 * 32 * D);
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        if (k + 3 < K) {
-            a[(k + 3) & 3][0] = lds16_a(ra.a[k + 3]);
-            a[(k + 3) & 3][1] = lds16_a(ra.a[k + 3] + 2 * 32 * D);
+        if (k + AHEAD < K) {
+            a[(k + AHEAD) % R][0] = lds16_a(ra.a[k + AHEAD]);
+            a[(k + AHEAD) % R][1] = lds16_a(ra.a[k + AHEAD] + 2 * 32 * D);
         }
-        c[0] = mfma32x32x16(a[k & 3][0], bf[k], c[0]);
-        c[1] = mfma32x32x16(a[k & 3][1], bf[k], c[1]);
+        c[0] = mfma32x32x16(a[k % R][0], bf[k], c[0]);
+        c[1] = mfma32x32x16(a[k % R][1], bf[k], c[1]);
     }
     // both chains end inside the region (a product used only later is otherwise sunk
     // past its closing fence)
     asm volatile("" : "+v"(c[0]), "+v"(c[1]));
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // DS reads of steps 0-2
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);   // DS reads of the first steps
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-        if (k + 3 < K) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // reads of step k+3
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA, chain 0
-        if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);     // vector work
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA, chain 1
-        if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+        if (k + AHEAD < K) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // reads of step k+AHEAD
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA, chain 0
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA, chain 1
     }
     __builtin_amdgcn_sched_barrier(0);
-}
-template <int D>
-__device__ __forceinline__ void qk_both(const RowAddr<D>& ra, const u32x4 (&bf)[D / 16], f32x16 (&c)[2]) {
-    qk_both<D, 0>(ra, bf, c, [] {});
 }
 
 // acc^T += T^T X over one query half qb (2 DB MFMAs into the DB accumulators), the
@@ -375,7 +367,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, uint16_t* smem, co
                 const bool mask = q0 < kw0 + 31 - wr || q0 + C::BQ > N || q0 + C::BQ - 1 > kw0 + wl;
                 {
                     const RowAddr<D> ra(ro, lds_addr(st));
-                    qk_both<D>(ra, bfr, x);
+                    qk_both<D, SPARSE ? 2 : 3>(ra, bfr, x);
                 }
                 if (mask) {
 #pragma unroll
@@ -423,7 +415,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, uint16_t* smem, co
                     for (int h2 = 0; h2 < 2; ++h2) praw[qb][h2] = *(const u32x4*)(pb + ((2 * qb + h2) * 64 + lane) * 4);
                 {
                     const RowAddr<D> ra(ro, lds_addr(st + C::NAT));
-                    qk_both<D>(ra, bfr, x);                                 // dP = dO V^T
+                    qk_both<D, SPARSE ? 2 : 3>(ra, bfr, x);                 // dP = dO V^T
                 }
                 f32x4 Dd[2][4];
 #pragma unroll
