@@ -190,6 +190,36 @@ __device__ __forceinline__ void qk_both(const RowAddr<D>& ra, const u32x4 (&bf)[
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// One query half of qk_both: the chain of half qb in a scheduling region of its own,
+// its A fragments read AHEAD MFMAs ahead, with the caller's independent vector work
+// `vec` placed NV instructions after each MFMA.
+template <int D, int AHEAD, int NV, typename F>
+__device__ __forceinline__ void qk_half_mixed(const RowAddr<D>& ra, const u32x4 (&bf)[D / 16], f32x16& c, int qb,
+                                              F&& vec) {
+    constexpr int K = D / 16;
+    constexpr int R = AHEAD + 1;
+    __builtin_amdgcn_sched_barrier(0);
+    vec();
+    c = zero16();
+    u32x4 a[R];
+#pragma unroll
+    for (int k = 0; k < AHEAD; ++k) a[k] = lds16_a(ra.a[k] + 2 * 32 * D * qb);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        if (k + AHEAD < K) a[(k + AHEAD) % R] = lds16_a(ra.a[k + AHEAD] + 2 * 32 * D * qb);
+        c = mfma32x32x16(a[k % R], bf[k], c);
+    }
+    asm volatile("" : "+v"(c));   // the chain ends inside the region
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);   // reads of the first MFMAs
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        if (k + AHEAD < K) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // read of MFMA k+AHEAD
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA k
+        if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);         // vector work
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // acc^T += T^T X over one query half qb (2 DB MFMAs into the DB accumulators), the
 // transposed A fragments read three MFMAs ahead (a ring of four), with the caller's
 // independent vector work `vec` placed NV instructions after each MFMA, in one
@@ -365,14 +395,6 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, uint16_t* smem, co
         if (act) {
             if constexpr (PV) {
                 const bool mask = q0 < kw0 + 31 - wr || q0 + C::BQ > N || q0 + C::BQ - 1 > kw0 + wl;
-                {
-                    const RowAddr<D> ra(ro, lds_addr(st));
-                    qk_both<D, SPARSE ? 2 : 3>(ra, bfr, x);
-                }
-                if (mask) {
-#pragma unroll
-                    for (int qb = 0; qb < 2; ++qb) mask_half(x[qb], q0 + 32 * qb + 4 * hh, key, N, wl, wr);
-                }
                 uint32_t* pb = pbuf + (mine & 1) * 4 * 64 * 16;
                 f32x4 L[2][4];
 #pragma unroll
@@ -392,7 +414,23 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, uint16_t* smem, co
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2) *(u32x4*)(pb + ((2 * qb + h2) * 64 + lane) * 4) = bf[qb][h2];
                 };
-                probs(0);
+                const RowAddr<D> ra(ro, lds_addr(st));
+                if (!SPARSE && !mask) {
+                    // S one query half at a time: half 0's exponentials run under half 1's
+                    // products (the empty asm pins their start inside that region)
+                    qk_half_mixed<D, 3, 0>(ra, bfr, x[0], 0, [] {});
+                    qk_half_mixed<D, 3, 5>(ra, bfr, x[1], 1, [&] {
+                        asm volatile("" : "+v"(x[0]));
+                        probs(0);
+                    });
+                } else {
+                    qk_both<D, SPARSE ? 2 : 3>(ra, bfr, x);
+                    if (mask) {
+#pragma unroll
+                        for (int qb = 0; qb < 2; ++qb) mask_half(x[qb], q0 + 32 * qb + 4 * hh, key, N, wl, wr);
+                    }
+                    probs(0);
+                }
                 hand_over(0);
                 __builtin_amdgcn_s_setprio(0);
                 const TrAddr<D> ta(to, lds_addr(st + C::NAT));
@@ -413,10 +451,6 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, uint16_t* smem, co
                 for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2) praw[qb][h2] = *(const u32x4*)(pb + ((2 * qb + h2) * 64 + lane) * 4);
-                {
-                    const RowAddr<D> ra(ro, lds_addr(st + C::NAT));
-                    qk_both<D, SPARSE ? 2 : 3>(ra, bfr, x);                 // dP = dO V^T
-                }
                 f32x4 Dd[2][4];
 #pragma unroll
                 for (int qb = 0; qb < 2; ++qb)
@@ -436,8 +470,20 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, uint16_t* smem, co
                         }
                     pack_half(x[qb], bf[qb]);
                 };
-                __builtin_amdgcn_s_setprio(2);
-                dsoft(0);
+                const RowAddr<D> ra(ro, lds_addr(st + C::NAT));
+                if constexpr (!SPARSE) {
+                    // dP = dO V^T one query half at a time, half 0's dS under half 1's products
+                    qk_half_mixed<D, 3, 0>(ra, bfr, x[0], 0, [] {});
+                    __builtin_amdgcn_s_setprio(2);
+                    qk_half_mixed<D, 3, 5>(ra, bfr, x[1], 1, [&] {
+                        asm volatile("" : "+v"(x[0]));
+                        dsoft(0);
+                    });
+                } else {
+                    qk_both<D, 2>(ra, bfr, x);                                // dP = dO V^T
+                    __builtin_amdgcn_s_setprio(2);
+                    dsoft(0);
+                }
                 const TrAddr<D> ta(to, lds_addr(st));
                 acc_half_mixed<D, 5>(ta, bf[0], acc, 0, [&] {                 // dK^T += Q^T dS, half 0
                     asm volatile("" : "+v"(x[1]));
