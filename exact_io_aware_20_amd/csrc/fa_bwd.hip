@@ -415,11 +415,11 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, uint16_t* smem, co
                     for (int h2 = 0; h2 < 2; ++h2) *(u32x4*)(pb + ((2 * qb + h2) * 64 + lane) * 4) = bf[qb][h2];
                 };
                 const RowAddr<D> ra(ro, lds_addr(st));
-                if (!SPARSE && !mask) {
+                if (!mask) {
                     // S one query half at a time: half 0's exponentials run under half 1's
                     // products (the empty asm pins their start inside that region)
-                    qk_half_mixed<D, 3, 0>(ra, bfr, x[0], 0, [] {});
-                    qk_half_mixed<D, 3, 5>(ra, bfr, x[1], 1, [&] {
+                    qk_half_mixed<D, SPARSE ? 2 : 3, 0>(ra, bfr, x[0], 0, [] {});
+                    qk_half_mixed<D, SPARSE ? 2 : 3, 5>(ra, bfr, x[1], 1, [&] {
                         asm volatile("" : "+v"(x[0]));
                         probs(0);
                     });
@@ -471,19 +471,13 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, uint16_t* smem, co
                     pack_half(x[qb], bf[qb]);
                 };
                 const RowAddr<D> ra(ro, lds_addr(st + C::NAT));
-                if constexpr (!SPARSE) {
-                    // dP = dO V^T one query half at a time, half 0's dS under half 1's products
-                    qk_half_mixed<D, 3, 0>(ra, bfr, x[0], 0, [] {});
-                    __builtin_amdgcn_s_setprio(2);
-                    qk_half_mixed<D, 3, 5>(ra, bfr, x[1], 1, [&] {
-                        asm volatile("" : "+v"(x[0]));
-                        dsoft(0);
-                    });
-                } else {
-                    qk_both<D, 2>(ra, bfr, x);                                // dP = dO V^T
-                    __builtin_amdgcn_s_setprio(2);
+                // dP = dO V^T one query half at a time, half 0's dS under half 1's products
+                qk_half_mixed<D, SPARSE ? 2 : 3, 0>(ra, bfr, x[0], 0, [] {});
+                __builtin_amdgcn_s_setprio(2);
+                qk_half_mixed<D, SPARSE ? 2 : 3, 5>(ra, bfr, x[1], 1, [&] {
+                    asm volatile("" : "+v"(x[0]));
                     dsoft(0);
-                }
+                });
                 const TrAddr<D> ta(to, lds_addr(st));
                 acc_half_mixed<D, 5>(ta, bf[0], acc, 0, [&] {                 // dK^T += Q^T dS, half 0
                     asm volatile("" : "+v"(x[1]));
