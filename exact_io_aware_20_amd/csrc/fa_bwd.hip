@@ -13,7 +13,8 @@
 // gfx950 mapping:
 //   * preprocess: per query row, D = dO . O and LSE in base-2 units, written to the
 //     workspace that the other two kernels read.
-//   * dK/dV kernel: a workgroup owns 128 keys of one KV head, 32 per pair of waves
+//   * dK/dV kernel: a workgroup owns a tile of 128 keys of one KV head (two such
+//     tiles, j and ntile-1-j, under the causal rule without a window), 32 per pair of waves
 //     (one forms S, P and dV, its partner dP, dS and dK one item later, P handed
 //     over through LDS in bf16), streaming 64-row tiles of Q and dO of every query head in
 //     the group through LDS by direct loads.  S = Q K^T is formed with the query on
@@ -287,7 +288,7 @@ __device__ __forceinline__ void acc_half(const TrAddr<D>& ta, const u32x4 (&bf)[
         for (int db = 0; db < D / 32; ++db) acc[db] = mfma32x32x16(ta.frag(db, 32 * qb + 16 * h2), bf[h2], acc[db]);
 }
 
-// dK/dV kernel.  A workgroup owns 128 keys of one KV head.  Wave w < 4 ("P/dV")
+// dK/dV kernel, one 128-key tile of one KV head.  Wave w < 4 ("P/dV")
 // and wave w + 4 ("dS/dK") own keys 32w .. 32w+31; the first computes S = Q K^T,
 // P = 2^(S*sl2 - LSE2) and dV^T += dO^T P for item it and hands P to its partner
 // through LDS, as the bf16 fragments the dV product uses; the partner, one item
