@@ -132,7 +132,10 @@ def test_forward_f32(shape, causal):
 
 
 BWD_SMALL = [(1, 1, 1, 1, 64), (1, 2, 1, 3, 128), (2, 2, 2, 17, 64), (1, 4, 1, 64, 128),
-             (1, 6, 2, 129, 64), (1, 4, 2, 200, 128), (1, 2, 2, 257, 64), (1, 3, 1, 384, 128)]
+             (1, 6, 2, 129, 64), (1, 4, 2, 200, 128), (1, 2, 2, 257, 64), (1, 3, 1, 384, 128),
+             # ragged, several causal key-tile pairs: 7 key tiles (odd: the middle one alone)
+             # and 8 (four pairs), with grouped query heads
+             (1, 4, 2, 777, 128), (2, 2, 1, 1000, 64)]
 
 
 @pytest.mark.parametrize("path", ["fused", "pair"])
