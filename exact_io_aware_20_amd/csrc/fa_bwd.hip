@@ -520,10 +520,12 @@ __device__ __forceinline__ void dkdv_role(const BwdParams& p, uint16_t* smem, co
     const int ntile_k = (p.N + C::BK - 1) / C::BK;
     const bool paired = !SPARSE && p.causal && p.window < 0;
     int head_kv, kt;
-    // paired workgroups all hold the same work, so the pairs of one head, side by side on
-    // one XCD, stream that head's Q/dO tiles through its L2 together, once
+    // Paired workgroups all hold the same work, and so do a window's tiles (one band
+    // each): the workgroups of one head, side by side on one XCD, then stream that head's
+    // Q/dO tiles through its L2 together.  Causal tiles without a pair differ in length,
+    // and there groups of four heads measured faster.
     map_block(blockIdx.x, gridDim.x, paired ? (ntile_k + 1) / 2 : ntile_k, p.B * p.Hkv, false, head_kv, kt,
-              paired ? 1 : 4);
+              (paired || p.window >= 0) ? 1 : 4);
     dkdv_tile<D, PV, SPARSE>(p, smem, list, list_n, wave, lane, head_kv, kt, false);
     const int kt2 = ntile_k - 1 - kt;
     if (paired && kt2 != kt) {
