@@ -126,31 +126,6 @@ __device__ __forceinline__ f32x16 qk_half(const RowAddr<D>& ra, const u32x4 (&bf
     return c;
 }
 
-// acc^T += T^T X over both query halves (16 MFMAs into the DB accumulators), in a
-// scheduling region of its own with each MFMA's transposed A fragment read three MFMAs
-// ahead (a ring of four), as qk_both does for the S-type products.
-template <int D>
-__device__ __forceinline__ void acc_both(const TrAddr<D>& ta, const u32x4 (&bf)[2][2], f32x16 (&acc)[D / 32]) {
-    constexpr int DB = D / 32;
-    constexpr int M = 2 * 2 * DB;   // (qb, h2, db)
-    __builtin_amdgcn_sched_barrier(0);
-    u32x4 a[4];
-#pragma unroll
-    for (int m = 0; m < 3; ++m) a[m] = ta.frag(m % DB, 16 * (m / DB));
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-        if (m + 3 < M) a[(m + 3) & 3] = ta.frag((m + 3) % DB, 16 * ((m + 3) / DB));
-        acc[m % DB] = mfma32x32x16(a[m & 3], bf[m / (2 * DB)][(m / DB) & 1], acc[m % DB]);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);   // transposed reads of MFMAs 0-2
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-        if (m + 3 < M) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // reads of MFMA m+3
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA m
-    }
-    __builtin_amdgcn_sched_barrier(0);
-}
-
 // Both query halves at once, in a scheduling region of their own: the two accumulation
 // chains interleaved, and each k-step's two A fragments read AHEAD steps ahead of their
 // MFMAs (a ring of AHEAD + 1 steps), so that an MFMA's operands are never the youngest

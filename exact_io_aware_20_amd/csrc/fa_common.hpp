@@ -61,7 +61,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ u32x4 ld_global16(const void* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ u32x4 lds16(const uint16_t* p) { return *(const u32x4*)p; }
-__device__ __forceinline__ u32x2 lds8(const uint16_t* p) { return *(const u32x2*)p; }
 __device__ __forceinline__ u32x4 zero_u4() { return u32x4{0u, 0u, 0u, 0u}; }
 __device__ __forceinline__ u32x4 cat(const u32x2& a, const u32x2& b) {
     return u32x4{a[0], a[1], b[0], b[1]};
