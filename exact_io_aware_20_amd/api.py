@@ -21,13 +21,15 @@ FA_STATUS = {
 }
 ENTRY_POINTS = ("fa_forward", "fa_forward_f32", "fa_forward_fp32_out", "fa_backward", "fa_backward_workspace_bytes",
                 "fa_backward_noalloc",
-                "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_backward_dkdv_dq",
+                "fa_backward_preprocess", "fa_backward_dkdv", "fa_backward_dq", "fa_backward_preprocess_dq",
+                "fa_backward_dkdv_dq",
                 "fa_backward_dq_convert", "fa_backward_fused", "fa_backward_fused_workspace_bytes",
                 "fa_decode_forward", "fa_decode_workspace_bytes", "fa_decode_split", "fa_decode_merge",
                 "fa_forward_window", "fa_backward_window", "fa_backward_dkdv_window", "fa_backward_dq_window",
+                "fa_backward_preprocess_dq_window",
                 "fa_decode_paged_forward", "fa_decode_paged_split", "fa_decode_paged_merge",
                 "fa_forward_blocksparse", "fa_backward_blocksparse", "fa_backward_dkdv_blocksparse",
-                "fa_backward_dq_blocksparse",
+                "fa_backward_dq_blocksparse", "fa_backward_preprocess_dq_blocksparse",
                 "fa_check_args", "fa_status_string")
 
 _lib = None
@@ -64,6 +66,8 @@ def load_library() -> ctypes.CDLL:
     lib.fa_backward_dkdv.restype = i
     lib.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, i, f, vp]
     lib.fa_backward_dq.restype = i
+    lib.fa_backward_preprocess_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_backward_preprocess_dq.restype = i
     lib.fa_backward_dkdv_dq.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, i, i, f, vp]
     lib.fa_backward_dkdv_dq.restype = i
     lib.fa_backward_fused.argtypes = lib.fa_backward.argtypes
@@ -89,6 +93,8 @@ def load_library() -> ctypes.CDLL:
     lib.fa_backward_dkdv_window.restype = i
     lib.fa_backward_dq_window.argtypes = [vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, i, i, f, vp]
     lib.fa_backward_dq_window.restype = i
+    lib.fa_backward_preprocess_dq_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, i, i, f, vp]
+    lib.fa_backward_preprocess_dq_window.restype = i
     for fn in (lib.fa_decode_paged_forward, lib.fa_decode_paged_split, lib.fa_decode_paged_merge):
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, i, i, i, f, vp]
         fn.restype = i
@@ -100,6 +106,9 @@ def load_library() -> ctypes.CDLL:
     lib.fa_backward_dkdv_blocksparse.restype = i
     lib.fa_backward_dq_blocksparse.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, i, i, f, vp]
     lib.fa_backward_dq_blocksparse.restype = i
+    lib.fa_backward_preprocess_dq_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, i, i, f,
+                                                          vp]
+    lib.fa_backward_preprocess_dq_blocksparse.restype = i
     lib.fa_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i]
     lib.fa_check_args.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -332,9 +341,10 @@ def backward_noalloc(q, k, v, o, do, lse, causal: bool, scale: float, dq=None, d
 def backward_steps(q, k, v, o, do, lse, causal: bool, scale: float, dq, dk, dv, workspace,
                    stream=None, steps=("pre", "dkdv", "dq"), window=None, block_mask=None):
     """Enqueue the named backward steps in order: "pre" (fa_backward_preprocess), then
-    "dkdv" and "dq" (fa_backward_dkdv / _dq, or their _window and _blocksparse forms), as
-    fa_backward runs them, or the fused alternative's "fused" and "convert"
-    (fa_backward_dkdv_dq, fa_backward_dq_convert; the workspace then needs
+    "dkdv" and "dq" (fa_backward_dkdv / _dq, or their _window and _blocksparse forms);
+    "pre_dq" (fa_backward_preprocess_dq and its forms: the preprocess and dQ in one
+    kernel), then "dkdv", as fa_backward runs them; or the fused alternative's "fused"
+    and "convert" (fa_backward_dkdv_dq, fa_backward_dq_convert; the workspace then needs
     fused_workspace_bytes, and "pre" also zeroes its accumulator).
 
     Preallocated outputs and workspace are required; this is the form the benchmark
@@ -372,6 +382,17 @@ def backward_steps(q, k, v, o, do, lse, causal: bool, scale: float, dq, dk, dv, 
             code = getattr(lib, fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
                                     workspace.data_ptr(), wsb, dk.data_ptr(), dv.data_ptr(),
                                     B, Hq, Hkv, N, d, int(causal), *extra, float(scale), st)
+        elif step == "pre_dq" and block_mask is not None:
+            code = lib.fa_backward_preprocess_dq_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                                             do.data_ptr(), lse.data_ptr(), workspace.data_ptr(), wsb,
+                                                             dq.data_ptr(), _layout(block_mask, N, q.device).data_ptr(),
+                                                             B, Hq, Hkv, N, d, int(causal), float(scale), st)
+        elif step == "pre_dq":
+            fn = "fa_backward_preprocess_dq" if window is None else "fa_backward_preprocess_dq_window"
+            extra = () if window is None else (int(window),)
+            code = getattr(lib, fn)(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                    lse.data_ptr(), workspace.data_ptr(), wsb, dq.data_ptr(),
+                                    B, Hq, Hkv, N, d, int(causal), *extra, float(scale), st)
         elif step == "dq":
             fn = "fa_backward_dq" if window is None else "fa_backward_dq_window"
             extra = () if window is None else (int(window),)
@@ -380,4 +401,5 @@ def backward_steps(q, k, v, o, do, lse, causal: bool, scale: float, dq, dk, dv, 
                                     B, Hq, Hkv, N, d, int(causal), *extra, float(scale), st)
         else:
             raise ValueError(step)
-        _check(f"fa_backward_{step}", code)
+        _check({"pre": "fa_backward_preprocess", "pre_dq": "fa_backward_preprocess_dq",
+                "fused": "fa_backward_dkdv_dq"}.get(step, f"fa_backward_{step}"), code)

@@ -78,9 +78,10 @@ fa_status check_fwd(const void* q, const void* k, const void* v, const void* o, 
 }
 
 // kAll: a whole backward call; kPre: the preprocess; kDkdv, kDq: the two kernels of the
-// deterministic pair (they read only the small workspace); kFused: the fused dK/dV/dQ
-// kernel (adds into the dQ accumulator); kConvert: accumulator -> dq.
-enum BwdStep { kAll, kPre, kDkdv, kDq, kFused, kConvert };
+// deterministic pair (they read only the small workspace); kPreDq: the dQ kernel that
+// forms the per-row terms itself and writes them to the workspace; kFused: the fused
+// dK/dV/dQ kernel (adds into the dQ accumulator); kConvert: accumulator -> dq.
+enum BwdStep { kAll, kPre, kDkdv, kDq, kPreDq, kFused, kConvert };
 
 fa_status check_bwd(BwdStep step, const void* q, const void* k, const void* v, const void* o,
                     const void* dO, const void* lse, const void* dq, const void* dk, const void* dv,
@@ -99,9 +100,9 @@ fa_status check_bwd(BwdStep step, const void* q, const void* k, const void* v, c
     // the preprocess also zeroes the fused accumulator when the workspace has room for it
     const size_t fused_need = bwd_fused_ws_bytes(B, Hq, N, d);
     const size_t ws_extent = step == kPre && ws_bytes >= fused_need ? fused_need : ws_need;
-    a[n++] = {workspace, ws_extent, step == kAll || step == kPre || step == kFused};
+    a[n++] = {workspace, ws_extent, step == kAll || step == kPre || step == kPreDq || step == kFused};
     if (step != kConvert) a[n++] = {dO, qb, false};
-    if (step == kAll || step == kPre) {
+    if (step == kAll || step == kPre || step == kPreDq) {
         a[n++] = {o, qb, false};
         a[n++] = {lse, lb, false};
     }
@@ -110,7 +111,7 @@ fa_status check_bwd(BwdStep step, const void* q, const void* k, const void* v, c
         a[n++] = {k, kb, false};
         a[n++] = {v, kb, false};
     }
-    if (step == kAll || step == kDq || step == kConvert) a[n++] = {dq, qb, true};
+    if (step == kAll || step == kDq || step == kPreDq || step == kConvert) a[n++] = {dq, qb, true};
     if (step == kAll || step == kDkdv || step == kFused) {
         a[n++] = {dk, kb, true};
         a[n++] = {dv, kb, true};
@@ -197,6 +198,7 @@ fa::BwdParams bwd_params(const void* q, const void* k, const void* v, const void
     p.block_mask = nullptr;
     p.scale = scale;
     p.scale_log2 = kernel_scale_log2(scale);
+    p.form_rows = 0;
     return p;
 }
 
@@ -205,13 +207,13 @@ int kernel_window(int window, int N) { return window < N - 1 ? window : -1; }
 
 fa_status launched(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
 
-// The backward as fa_backward runs it: preprocess (D, LSE in base 2), then the dK/dV and
-// dQ kernels of the deterministic pair.
+// The backward as fa_backward runs it: the dQ kernel, which forms the per-row terms (D,
+// LSE in base 2) itself, bit for bit as the preprocess does, and writes them to the
+// workspace; then the dK/dV kernel, which reads them.
 fa_status pair_backward(const fa::BwdParams& p, int d, hipStream_t stream) {
     fa_status s;
-    if ((s = launched(fa::launch_bwd_pre(p, d, stream))) != FA_OK) return s;
-    if ((s = launched(fa::launch_bwd_dkdv(p, d, stream))) != FA_OK) return s;
-    return launched(fa::launch_bwd_dq(p, d, stream));
+    if ((s = launched(fa::launch_bwd_dq_rows(p, d, stream))) != FA_OK) return s;
+    return launched(fa::launch_bwd_dkdv(p, d, stream));
 }
 
 // The fused alternative: the workspace's dQ accumulator follows the per-row terms.
@@ -452,9 +454,7 @@ fa_status fa_backward_noalloc(const void* q, const void* k, const void* v, const
     float* ws = nullptr;
     if ((s = launched(fa::bwd_scratch(stream, &ws))) != FA_OK) return s;
     const fa::BwdParams p = bwd_params(q, k, v, o, dO, lse, dq, dk, dv, ws, B, Hq, Hkv, N, causal, scale);
-    if ((s = launched(fa::launch_bwd_pre(p, d, stream))) != FA_OK) return s;
-    if ((s = launched(fa::launch_bwd_dkdv(p, d, stream))) != FA_OK) return s;
-    return launched(fa::launch_bwd_dq(p, d, stream));
+    return pair_backward(p, d, stream);
 }
 
 fa_status fa_forward_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
@@ -506,6 +506,19 @@ fa_status fa_backward_dq_window(const void* q, const void* k, const void* v, con
     return launched(fa::launch_bwd_dq(p, d, stream));
 }
 
+fa_status fa_backward_preprocess_dq_window(const void* q, const void* k, const void* v, const void* o,
+                                           const void* dO, const float* lse, void* workspace, size_t workspace_bytes,
+                                           void* dq, int B, int Hq, int Hkv, int N, int d, int causal, int window,
+                                           float scale, hipStream_t stream) {
+    if (window < 0) return FA_ERR_WINDOW;
+    fa_status s = check_bwd(kPreDq, q, k, v, o, dO, lse, dq, nullptr, nullptr, workspace, workspace_bytes, B, Hq,
+                            Hkv, N, d, causal, scale);
+    if (s != FA_OK) return s;
+    fa::BwdParams p = bwd_params(q, k, v, o, dO, lse, dq, nullptr, nullptr, workspace, B, Hq, Hkv, N, causal, scale);
+    p.window = kernel_window(window, N);
+    return launched(fa::launch_bwd_dq_rows(p, d, stream));
+}
+
 // Block-sparse calls: the layout must be present and cover at most 2048 x 2048
 // blocks; it is an input of every step, so no output may overlap it.
 static fa_status check_layout(const void* block_mask, const void* const* outs, const uintptr_t* out_bytes, int nout,
@@ -538,7 +551,9 @@ static fa_status bwd_blocksparse(int steps, const void* q, const void* k, const 
                                  const void* dO, const float* lse, void* dq, void* dk, void* dv,
                                  const unsigned char* block_mask, void* workspace, size_t workspace_bytes, int B,
                                  int Hq, int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
-    const BwdStep step = steps == 7 ? kAll : (steps == 2 ? kDkdv : kDq);
+    // steps: 7 the whole call, 2 the dK/dV step, 4 the dQ step, 5 the dQ step that forms
+    // the per-row terms (the preprocess and dQ in one kernel)
+    const BwdStep step = steps == 7 ? kAll : (steps == 2 ? kDkdv : (steps == 5 ? kPreDq : kDq));
     fa_status s = check_bwd(step, q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N, d,
                             causal, scale);
     if (s != FA_OK) return s;
@@ -551,10 +566,10 @@ static fa_status bwd_blocksparse(int steps, const void* q, const void* k, const 
     if ((s = check_layout(block_mask, outs, ob, 4, N)) != FA_OK) return s;
     fa::BwdParams p = bwd_params(q, k, v, o, dO, lse, dq, dk, dv, workspace, B, Hq, Hkv, N, causal, scale);
     p.block_mask = block_mask;
-    if ((steps & 1) && (s = launched(fa::launch_bwd_pre(p, d, stream))) != FA_OK) return s;
-    if ((steps & 2) && (s = launched(fa::launch_bwd_dkdv(p, d, stream))) != FA_OK) return s;
-    if (steps & 4) return launched(fa::launch_bwd_dq(p, d, stream));
-    return FA_OK;
+    if (steps == 7) return pair_backward(p, d, stream);
+    if (steps == 2) return launched(fa::launch_bwd_dkdv(p, d, stream));
+    if (steps == 5) return launched(fa::launch_bwd_dq_rows(p, d, stream));
+    return launched(fa::launch_bwd_dq(p, d, stream));
 }
 
 fa_status fa_backward_blocksparse(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -579,6 +594,15 @@ fa_status fa_backward_dq_blocksparse(const void* q, const void* k, const void* v
                                      int causal, float scale, hipStream_t stream) {
     return bwd_blocksparse(4, q, k, v, nullptr, dO, nullptr, dq, nullptr, nullptr, block_mask, (void*)workspace,
                            workspace_bytes, B, Hq, Hkv, N, d, causal, scale, stream);
+}
+
+fa_status fa_backward_preprocess_dq_blocksparse(const void* q, const void* k, const void* v, const void* o,
+                                                const void* dO, const float* lse, void* workspace,
+                                                size_t workspace_bytes, void* dq, const unsigned char* block_mask,
+                                                int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                                                hipStream_t stream) {
+    return bwd_blocksparse(5, q, k, v, o, dO, lse, dq, nullptr, nullptr, block_mask, workspace, workspace_bytes, B,
+                           Hq, Hkv, N, d, causal, scale, stream);
 }
 
 fa_status fa_backward_preprocess(const void* o, const void* dO, const float* lse, void* workspace,
@@ -612,6 +636,17 @@ fa_status fa_backward_dq(const void* q, const void* k, const void* v, const void
     const fa::BwdParams p =
         bwd_params(q, k, v, nullptr, dO, nullptr, dq, nullptr, nullptr, workspace, B, Hq, Hkv, N, causal, scale);
     return launched(fa::launch_bwd_dq(p, d, stream));
+}
+
+fa_status fa_backward_preprocess_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                                    const float* lse, void* workspace, size_t workspace_bytes, void* dq, int B,
+                                    int Hq, int Hkv, int N, int d, int causal, float scale, hipStream_t stream) {
+    fa_status s = check_bwd(kPreDq, q, k, v, o, dO, lse, dq, nullptr, nullptr, workspace, workspace_bytes, B, Hq,
+                            Hkv, N, d, causal, scale);
+    if (s != FA_OK) return s;
+    const fa::BwdParams p =
+        bwd_params(q, k, v, o, dO, lse, dq, nullptr, nullptr, workspace, B, Hq, Hkv, N, causal, scale);
+    return launched(fa::launch_bwd_dq_rows(p, d, stream));
 }
 
 fa_status fa_backward_dkdv_dq(const void* q, const void* k, const void* v, const void* dO, void* workspace,

@@ -1001,8 +1001,40 @@ void fa_bwd_dq_kernel(BwdParams p) {
         qf[c] = ok ? ld_global16((const uint16_t*)p.q + qoff + (size_t)q * D + 16 * c + 8 * hh) : zero_u4();
         gf[c] = ok ? ld_global16((const uint16_t*)p.dO + qoff + (size_t)q * D + 16 * c + 8 * hh) : zero_u4();
     }
-    const float lse2 = ok ? p.lse2[(size_t)head * N + q] : 0.f;
-    const float dd = ok ? p.dsum[(size_t)head * N + q] : 0.f;
+    float lse2, dd;
+    if (p.form_rows) {
+        // The per-row terms formed here, bit for bit as fa_bwd_pre_kernel forms them:
+        // D = dO . O as one fma chain per 8-element chunk j = 2c + hh, the chunks then
+        // summed pairwise over j ^ D/16, ..., j ^ 2 (in this lane) and j ^ 1 (the other
+        // half of the row, lane ^ 32); LSE in base 2, +inf for a row that saw no key.
+        // Written to the workspace for the dK/dV kernel.
+        float part[C::DC];
+#pragma unroll
+        for (int c = 0; c < C::DC; ++c) {
+            const u32x4 a = ok ? ld_global16((const uint16_t*)p.o + qoff + (size_t)q * D + 16 * c + 8 * hh) : zero_u4();
+            float acc = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                acc = __builtin_fmaf(bf16_lo(a[w]), bf16_lo(gf[c][w]), acc);
+                acc = __builtin_fmaf(bf16_hi(a[w]), bf16_hi(gf[c][w]), acc);
+            }
+            part[c] = acc;
+        }
+#pragma unroll
+        for (int m = C::DC / 2; m >= 1; m >>= 1)
+#pragma unroll
+            for (int c = 0; c < m; ++c) part[c] = part[c] + part[c + m];
+        dd = part[0] + __shfl_xor(part[0], 32);
+        const float l = ok ? p.lse[(size_t)head * N + q] : 0.f;
+        lse2 = l == kNegInf ? __builtin_huge_valf() : l * kLog2e;
+        if (ok && hh == 0) {
+            p.dsum[(size_t)head * N + q] = dd;
+            p.lse2[(size_t)head * N + q] = lse2;
+        }
+    } else {
+        lse2 = ok ? p.lse2[(size_t)head * N + q] : 0.f;
+        dd = ok ? p.dsum[(size_t)head * N + q] : 0.f;
+    }
     f32x16 dqt[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) dqt[db] = zero16();
@@ -1218,6 +1250,11 @@ hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t stream) {
 }
 hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t stream) {
     return d == 64 ? launch_dq<64>(p, stream) : launch_dq<128>(p, stream);
+}
+hipError_t launch_bwd_dq_rows(const BwdParams& p, int d, hipStream_t stream) {
+    BwdParams r = p;
+    r.form_rows = 1;
+    return d == 64 ? launch_dq<64>(r, stream) : launch_dq<128>(r, stream);
 }
 
 }  // namespace fa

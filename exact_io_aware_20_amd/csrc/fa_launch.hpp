@@ -58,6 +58,8 @@ struct BwdParams {
     const uint8_t* block_mask;   // as in FwdParams
     float scale;
     float scale_log2;
+    int form_rows;      // dQ kernel: form the per-row terms (dsum, lse2) from o, dO and lse
+                        // and write them, instead of reading the preprocess's
 };
 
 // Decode: Nq queries per head against Nk cached keys, the key range cut into
@@ -107,5 +109,6 @@ hipError_t launch_bwd_dkdv(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_bwd_fused(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_bwd_dq_convert(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, int d, hipStream_t stream);
+hipError_t launch_bwd_dq_rows(const BwdParams& p, int d, hipStream_t stream);   // dQ forming the per-row terms
 
 }  // namespace fa

@@ -127,8 +127,9 @@ size_t fa_backward_workspace_bytes(int B, int Hq, int N);
  * dk and dv of a KV head are the sums over the Hq/Hkv query heads of its group.
  * workspace: device memory of at least fa_backward_workspace_bytes(B,Hq,N)
  * bytes (passed in workspace_bytes), 16-byte aligned, clobbered by the call.
- * It enqueues fa_backward_preprocess, fa_backward_dkdv and fa_backward_dq; every
- * output is bit-reproducible from run to run.
+ * It enqueues fa_backward_preprocess_dq, then fa_backward_dkdv; the results are
+ * bit-identical to fa_backward_preprocess + fa_backward_dkdv + fa_backward_dq, and
+ * every output is bit-reproducible from run to run.
  * Errors: those of fa_forward, and FA_ERR_WORKSPACE (NULL, misaligned or smaller
  * than required); the workspace may overlap no tensor argument (FA_ERR_ALIAS).
  */
@@ -192,13 +193,19 @@ fa_status fa_backward_noalloc(const void* q, const void* k, const void* v, const
  *     alternative's dQ accumulator.
  *   fa_backward_dkdv: dk, dv from q, k, v, dO and the preprocessed workspace;
  *   fa_backward_dq:   dq from q, k, v, dO and the preprocessed workspace
- *     (these two only read the workspace and may run concurrently on two streams).
+ *     (these two only read the workspace and may run concurrently on two streams);
+ *   fa_backward_preprocess_dq: fa_backward_preprocess and fa_backward_dq in one
+ *     kernel: each dQ workgroup forms the per-row terms of its own rows (from o, dO and
+ *     lse, bit for bit as fa_backward_preprocess does, without the fused alternative's
+ *     accumulator), writes them to the workspace and uses them; fa_backward_dkdv may
+ *     follow once it has completed.  This is the order fa_backward takes.
  *   fa_backward_dkdv_dq (fused alternative, workspace of
  *     fa_backward_fused_workspace_bytes): dk, dv, and every row's dQ contribution added
  *     (unscaled, fp32) into the accumulator, which it requires zeroed by the preprocess;
  *   fa_backward_dq_convert: dq = scale * accumulator, rounded to bf16.
  * The kernels after the preprocess read the saved statistic only through the
- * workspace, so it must come from fa_backward_preprocess of the same o, dO and lse.
+ * workspace, so it must come from fa_backward_preprocess (or
+ * fa_backward_preprocess_dq) of the same o, dO and lse.
  */
 fa_status fa_backward_preprocess(const void* o, const void* dO, const float* lse, void* workspace,
                                  size_t workspace_bytes, int B, int Hq, int N, int d, hipStream_t stream);
@@ -210,6 +217,10 @@ fa_status fa_backward_dq(const void* q, const void* k, const void* v, const void
                          const void* workspace, size_t workspace_bytes,
                          void* dq, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                          hipStream_t stream);
+fa_status fa_backward_preprocess_dq(const void* q, const void* k, const void* v, const void* o,
+                                    const void* dO, const float* lse, void* workspace,
+                                    size_t workspace_bytes, void* dq, int B, int Hq, int Hkv, int N,
+                                    int d, int causal, float scale, hipStream_t stream);
 fa_status fa_backward_dkdv_dq(const void* q, const void* k, const void* v, const void* dO,
                               void* workspace, size_t workspace_bytes, void* dk, void* dv,
                               int B, int Hq, int Hkv, int N, int d, int causal, float scale,
@@ -226,7 +237,8 @@ fa_status fa_backward_dq_convert(const void* workspace, size_t workspace_bytes, 
  * a window of N - 1 or more is no restriction.  Tiles wholly outside the band are
  * neither loaded nor computed.  Other arguments, layouts and errors are those of the
  * calls without a window; the backward takes lse from fa_forward_window with the same
- * window, and the dK/dV and dQ steps take the workspace of fa_backward_preprocess.
+ * window, the dK/dV and dQ steps take the workspace of fa_backward_preprocess, and
+ * fa_backward_preprocess_dq_window is fa_backward_preprocess_dq with the window.
  */
 fa_status fa_forward_window(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int Hq, int Hkv, int N, int d, int causal, int window, float scale,
@@ -244,6 +256,11 @@ fa_status fa_backward_dq_window(const void* q, const void* k, const void* v, con
                                 const void* workspace, size_t workspace_bytes,
                                 void* dq, int B, int Hq, int Hkv, int N, int d, int causal,
                                 int window, float scale, hipStream_t stream);
+fa_status fa_backward_preprocess_dq_window(const void* q, const void* k, const void* v,
+                                           const void* o, const void* dO, const float* lse,
+                                           void* workspace, size_t workspace_bytes, void* dq,
+                                           int B, int Hq, int Hkv, int N, int d, int causal,
+                                           int window, float scale, hipStream_t stream);
 
 
 /*
@@ -256,8 +273,9 @@ fa_status fa_backward_dq_window(const void* q, const void* k, const void* v, con
  * Blocks whose byte is 0 are neither loaded nor computed.  A query that sees no key
  * gets O = 0 and LSE = -inf, and contributes nothing to the gradients.  Other
  * arguments, layouts and errors are those of the dense calls; the backward takes lse
- * from fa_forward_blocksparse with the same layout, and the dK/dV and dQ steps take
- * the workspace of fa_backward_preprocess.
+ * from fa_forward_blocksparse with the same layout, the dK/dV and dQ steps take
+ * the workspace of fa_backward_preprocess, and fa_backward_preprocess_dq_blocksparse
+ * is fa_backward_preprocess_dq with the layout.
  */
 fa_status fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
                                  const unsigned char* block_mask,
@@ -278,6 +296,12 @@ fa_status fa_backward_dq_blocksparse(const void* q, const void* k, const void* v
                                      const unsigned char* block_mask,
                                      int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                                      hipStream_t stream);
+fa_status fa_backward_preprocess_dq_blocksparse(const void* q, const void* k, const void* v,
+                                                const void* o, const void* dO, const float* lse,
+                                                void* workspace, size_t workspace_bytes, void* dq,
+                                                const unsigned char* block_mask,
+                                                int B, int Hq, int Hkv, int N, int d, int causal,
+                                                float scale, hipStream_t stream);
 
 /*
  * Decode forward: Nq new queries per head against a cache of Nk keys and values.

@@ -24,6 +24,7 @@ hipError_t launch_decode(const DecodeParams&, int, int, bool, hipStream_t) { ret
 hipError_t launch_bwd_pre(const BwdParams&, int, hipStream_t) { return counted(); }
 hipError_t launch_bwd_dkdv(const BwdParams&, int, hipStream_t) { return counted(); }
 hipError_t launch_bwd_dq(const BwdParams&, int, hipStream_t) { return counted(); }
+hipError_t launch_bwd_dq_rows(const BwdParams&, int, hipStream_t) { return counted(); }
 hipError_t launch_bwd_fused(const BwdParams&, int, hipStream_t) { return counted(); }
 hipError_t launch_bwd_dq_convert(const BwdParams&, int, hipStream_t) { return counted(); }
 // a fixed, aligned stand-in address (never dereferenced: the launchers are stand-ins)

@@ -156,6 +156,12 @@ def test_backward_steps_reject_before_launch():
     assert lib.fa_backward_dkdv(Q, K, V, dO, ws, need, dk, dv, 1, 2, 1, 16, 64, 2, 0.1, None) == 7
     assert lib.fa_backward_dq(Q, K, V, dO, ws, need, Q, 1, 2, 1, 16, 64, 1, 0.1, None) == 9
     assert lib.fa_backward_dq(Q, K, V, dO, ws, need, dq, 1, 3, 2, 16, 64, 1, 0.1, None) == 3
+    # the preprocess and dQ in one kernel: reads o, dO, lse, q, k, v; writes the workspace and dq
+    assert lib.fa_backward_preprocess_dq(Q, K, V, O, dO, None, ws, need, dq, 1, 2, 1, 16, 64, 1, 0.1, None) == 1
+    assert lib.fa_backward_preprocess_dq(Q, K, V, O, dO, lse, ws, need - 4, dq, 1, 2, 1, 16, 64, 1, 0.1, None) == 8
+    assert lib.fa_backward_preprocess_dq(Q, K, V, O, dO, lse, lse, need, dq, 1, 2, 1, 16, 64, 1, 0.1, None) == 9
+    assert lib.fa_backward_preprocess_dq(Q, K, V, O, dO, lse, ws, need, O, 1, 2, 1, 16, 64, 1, 0.1, None) == 9
+    assert lib.fa_backward_preprocess_dq(Q, K, V, O, dO, lse, ws, need, dq, 1, 3, 2, 16, 64, 1, 0.1, None) == 3
 
 
 def test_decode_workspace_bytes():
@@ -301,10 +307,10 @@ def test_every_entry_point_launches_only_after_validation():
          lambda: lib.fa_forward_fp32_out(Q, K, V, L - 64, L, 2, 4, 2, 300, 128, 1, 0.1, None)),
         ("fa_forward_f32", 1, lambda c: lib.fa_forward_f32(Q, K, V, O, L, 2, 4, 2, 300, 64, c, 0.1, None),
          lambda: lib.fa_forward_f32(Q, K, V, Q, L, 2, 4, 2, 300, 64, 1, 0.1, None)),
-        ("fa_backward", 3, lambda c: lib.fa_backward(Q, K, V, O, dO, L, dq, dk, dv, ws, need, 2, 4, 2, 300, 128, c,
+        ("fa_backward", 2, lambda c: lib.fa_backward(Q, K, V, O, dO, L, dq, dk, dv, ws, need, 2, 4, 2, 300, 128, c,
                                                       0.1, None),
          lambda: lib.fa_backward(Q, K, V, O, dO, L, dq, dk, dv, ws, need - 1, 2, 4, 2, 300, 128, 1, 0.1, None)),
-        ("fa_backward_noalloc", 3, lambda c: lib.fa_backward_noalloc(Q, K, V, O, dO, L, dq, dk, dv, 2, 4, 2, 300,
+        ("fa_backward_noalloc", 2, lambda c: lib.fa_backward_noalloc(Q, K, V, O, dO, L, dq, dk, dv, 2, 4, 2, 300,
                                                                       128, c, 0.1, None),
          lambda: lib.fa_backward_noalloc(Q, K, V, O, dO, L, dq, dk, dv, 8, 32, 32, 8193, 128, 1, 0.1, None)),
         ("fa_backward_preprocess", 1, lambda c: lib.fa_backward_preprocess(O, dO, L, ws, need, 2, 4, 300, 128, None),
@@ -315,6 +321,9 @@ def test_every_entry_point_launches_only_after_validation():
         ("fa_backward_dq", 1, lambda c: lib.fa_backward_dq(Q, K, V, dO, ws, need, dq, 2, 4, 2, 300, 64, c, 0.1,
                                                             None),
          lambda: lib.fa_backward_dq(Q, K, V, dO, ws, need, dq, 2, 4, 3, 300, 64, 1, 0.1, None)),
+        ("fa_backward_preprocess_dq", 1,
+         lambda c: lib.fa_backward_preprocess_dq(Q, K, V, O, dO, L, ws, need, dq, 2, 4, 2, 300, 128, c, 0.1, None),
+         lambda: lib.fa_backward_preprocess_dq(Q, K, V, O, dO, L, ws, need, dq, 2, 4, 3, 300, 128, 1, 0.1, None)),
         ("fa_backward_fused", 3, lambda c: lib.fa_backward_fused(Q, K, V, O, dO, L, dq, dk, dv, ws, fneed, 2, 4, 2,
                                                                   300, 128, c, 0.1, None),
          lambda: lib.fa_backward_fused(Q, K, V, O, dO, L, dq, dk, dv, ws, need, 2, 4, 2, 300, 128, 1, 0.1, None)),
@@ -326,7 +335,7 @@ def test_every_entry_point_launches_only_after_validation():
         ("fa_forward_window", 1, lambda c: lib.fa_forward_window(Q, K, V, O, L, 2, 4, 2, 300, 128, c, 17, 0.1,
                                                                   None),
          lambda: lib.fa_forward_window(Q, K, V, O, L, 2, 4, 2, 300, 128, 1, -2, 0.1, None)),
-        ("fa_backward_window", 3, lambda c: lib.fa_backward_window(Q, K, V, O, dO, L, dq, dk, dv, ws, need, 2, 4, 2,
+        ("fa_backward_window", 2, lambda c: lib.fa_backward_window(Q, K, V, O, dO, L, dq, dk, dv, ws, need, 2, 4, 2,
                                                                     300, 128, c, 17, 0.1, None),
          lambda: lib.fa_backward_window(Q, K, V, O, dO, L, dq, dk, dv, ws, need, 2, 4, 2, 300, 128, 1, 17,
                                         float("inf"), None)),
@@ -336,10 +345,15 @@ def test_every_entry_point_launches_only_after_validation():
         ("fa_backward_dq_window", 1, lambda c: lib.fa_backward_dq_window(Q, K, V, dO, ws, need, dq, 2, 4, 2, 300,
                                                                           64, c, 5, 0.1, None),
          lambda: lib.fa_backward_dq_window(Q, K, V, dO, None, need, dq, 2, 4, 2, 300, 64, 1, 5, 0.1, None)),
+        ("fa_backward_preprocess_dq_window", 1,
+         lambda c: lib.fa_backward_preprocess_dq_window(Q, K, V, O, dO, L, ws, need, dq, 2, 4, 2, 300, 64, c, 5, 0.1,
+                                                        None),
+         lambda: lib.fa_backward_preprocess_dq_window(Q, K, V, O, dO, L, ws, need, dq, 2, 4, 2, 300, 64, 1, -1, 0.1,
+                                                      None)),
         ("fa_forward_blocksparse", 1, lambda c: lib.fa_forward_blocksparse(Q, K, V, O, L, BM, 2, 4, 2, 300, 128, c,
                                                                             0.1, None),
          lambda: lib.fa_forward_blocksparse(Q, K, V, O, L, L, 2, 4, 2, 300, 128, 1, 0.1, None)),
-        ("fa_backward_blocksparse", 3, lambda c: lib.fa_backward_blocksparse(Q, K, V, O, dO, L, dq, dk, dv, BM, ws,
+        ("fa_backward_blocksparse", 2, lambda c: lib.fa_backward_blocksparse(Q, K, V, O, dO, L, dq, dk, dv, BM, ws,
                                                                               need, 2, 4, 2, 300, 128, c, 0.1, None),
          lambda: lib.fa_backward_blocksparse(Q, K, V, O, dO, L, dq, dk, dv, dk, ws, need, 2, 4, 2, 300, 128, 1,
                                              0.1, None)),
@@ -351,6 +365,11 @@ def test_every_entry_point_launches_only_after_validation():
         ("fa_backward_dq_blocksparse", 1,
          lambda c: lib.fa_backward_dq_blocksparse(Q, K, V, dO, ws, need, dq, BM, 2, 4, 2, 300, 64, c, 0.1, None),
          lambda: lib.fa_backward_dq_blocksparse(Q, K, V, dO, ws, need, dq, BM, 2, 4, 2, 300, 64, 5, 0.1, None)),
+        ("fa_backward_preprocess_dq_blocksparse", 1,
+         lambda c: lib.fa_backward_preprocess_dq_blocksparse(Q, K, V, O, dO, L, ws, need, dq, BM, 2, 4, 2, 300, 64, c,
+                                                             0.1, None),
+         lambda: lib.fa_backward_preprocess_dq_blocksparse(Q, K, V, O, dO, L, ws, need, dq, None, 2, 4, 2, 300, 64, 1,
+                                                           0.1, None)),
         ("fa_decode_forward", 1, lambda c: lib.fa_decode_forward(Q, K, V, O, L, ws, dneed, 2, 4, 2, 3, 1000, 128, c,
                                                                   0.1, None),
          lambda: lib.fa_decode_forward(Q, K, V, O, L, ws, dneed - 1, 2, 4, 2, 3, 1000, 128, 1, 0.1, None)),

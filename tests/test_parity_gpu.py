@@ -142,7 +142,7 @@ BWD_SMALL = [(1, 1, 1, 1, 64), (1, 2, 1, 3, 128), (2, 2, 2, 17, 64), (1, 4, 1, 6
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("shape", BWD_SMALL, ids=lambda s: "x".join(map(str, s)))
 def test_backward_bf16_small(shape, causal, path):
-    # "pair": fa_backward (preprocess, dK/dV kernel, dQ kernel); "fused": the alternative
+    # "pair": fa_backward (dQ kernel forming the per-row terms, then dK/dV); "fused": the alternative
     # fa_backward_fused (dK/dV and dQ in one kernel, dQ by fp32 atomic adds)
     B, Hq, Hkv, N, d = shape
     host, g = make(*shape, seed=9000 + N + d, with_do=True)
@@ -191,8 +191,8 @@ def _bits(t):
 
 
 def test_bitwise_deterministic():
-    # ten runs of the forward and of the deterministic backward (preprocess, dK/dV
-    # kernel, dQ kernel) give identical bits
+    # ten runs of the forward and of the deterministic backward (dQ kernel forming the
+    # per-row terms, then dK/dV) give identical bits
     B, Hq, Hkv, N, d = 2, 4, 2, 333, 128
     host, g = make(B, Hq, Hkv, N, d, seed=9600, with_do=True)
     ws = torch.empty(api.workspace_bytes(B, Hq, N), dtype=torch.uint8, device=dev())
@@ -408,8 +408,8 @@ def test_backward_whole_tensor_xcd_remap(shape, causal):
 
 
 def test_backward_steps_match_whole_call():
-    # fa_backward equals its three steps called one by one, with dK/dV and dQ on two
-    # streams after the preprocess, bit for bit; the fused alternative equals its own
+    # fa_backward equals the three separate steps called one by one, with dK/dV and dQ on
+    # two streams after the preprocess, bit for bit; the fused alternative equals its own
     # steps (dK and dV bit for bit, dQ up to the order of its fp32 atomic adds)
     B, Hq, Hkv, N, d = 1, 4, 2, 300, 128
     host, g = make(B, Hq, Hkv, N, d, seed=9950, with_do=True)
@@ -480,6 +480,38 @@ def test_preprocess_workspace_contents():
     assert np.array_equal(w[rows:2 * rows], lse2)
     acc0 = ((8 * rows + 255) // 256) * 256 // 4
     assert (w[acc0:acc0 + rows * d] == 0).all()
+
+
+@pytest.mark.parametrize("shape,causal,mode", [
+    ((1, 4, 2, 300, 128), True, "dense"), ((1, 4, 2, 300, 128), False, "dense"),
+    ((2, 3, 3, 77, 64), True, "dense"), ((1, 2, 1, 1000, 128), False, "dense"),
+    ((1, 4, 2, 700, 128), True, "window"), ((1, 4, 2, 700, 64), True, "sparse")])
+def test_preprocess_dq_equals_preprocess_then_dq(shape, causal, mode):
+    # fa_backward_preprocess_dq (the order fa_backward takes) writes the per-row terms of
+    # the workspace and dq exactly as fa_backward_preprocess followed by fa_backward_dq do,
+    # bit for bit, whatever the workspace and dq held before (two different fills)
+    B, Hq, Hkv, N, d = shape
+    host, g = make(B, Hq, Hkv, N, d, seed=9970 + N + d, with_do=True)
+    kw = {}
+    if mode == "window":
+        kw["window"] = 150
+    elif mode == "sparse":
+        kw["block_mask"] = inputs.random_layout(N, 0.4, 9971).to(dev())
+    o, lse = api.forward(g["q"], g["k"], g["v"], causal, 0.11, **kw)
+    rows = B * Hq * N
+    nws = api.workspace_bytes(B, Hq, N)
+    ws1 = torch.full((nws,), 0xFF, dtype=torch.uint8, device=dev())
+    ws2 = torch.full((nws,), 0x7F, dtype=torch.uint8, device=dev())
+    dq1, dq2 = poisoned(g["q"].shape, torch.bfloat16), torch.zeros_like(g["q"])
+    dk, dv = torch.empty_like(g["k"]), torch.empty_like(g["v"])
+    api.backward_steps(g["q"], g["k"], g["v"], o, g["do"], lse, causal, 0.11, dq1, dk, dv, ws1,
+                       steps=("pre", "dq"), **kw)
+    api.backward_steps(g["q"], g["k"], g["v"], o, g["do"], lse, causal, 0.11, dq2, dk, dv, ws2,
+                       steps=("pre_dq",), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(ws1[:8 * rows], ws2[:8 * rows])
+    assert torch.equal(dq1.view(torch.int16), dq2.view(torch.int16))
+    all_finite(dq=dq2)
 
 
 def test_tiny_f32_workload():
