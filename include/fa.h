@@ -275,7 +275,9 @@ fa_status fa_backward_preprocess_dq_window(const void* q, const void* k, const v
  * arguments, layouts and errors are those of the dense calls; the backward takes lse
  * from fa_forward_blocksparse with the same layout, the dK/dV and dQ steps take
  * the workspace of fa_backward_preprocess, and fa_backward_preprocess_dq_blocksparse
- * is fa_backward_preprocess_dq with the layout.
+ * is fa_backward_preprocess_dq with the layout.  fa_backward_blocksparse enqueues
+ * fa_backward_preprocess, then the dK/dV and dQ steps (same results as the order
+ * fa_backward takes, bit for bit).
  */
 fa_status fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
                                  const unsigned char* block_mask,

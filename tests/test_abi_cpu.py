@@ -353,7 +353,7 @@ def test_every_entry_point_launches_only_after_validation():
         ("fa_forward_blocksparse", 1, lambda c: lib.fa_forward_blocksparse(Q, K, V, O, L, BM, 2, 4, 2, 300, 128, c,
                                                                             0.1, None),
          lambda: lib.fa_forward_blocksparse(Q, K, V, O, L, L, 2, 4, 2, 300, 128, 1, 0.1, None)),
-        ("fa_backward_blocksparse", 2, lambda c: lib.fa_backward_blocksparse(Q, K, V, O, dO, L, dq, dk, dv, BM, ws,
+        ("fa_backward_blocksparse", 3, lambda c: lib.fa_backward_blocksparse(Q, K, V, O, dO, L, dq, dk, dv, BM, ws,
                                                                               need, 2, 4, 2, 300, 128, c, 0.1, None),
          lambda: lib.fa_backward_blocksparse(Q, K, V, O, dO, L, dq, dk, dv, dk, ws, need, 2, 4, 2, 300, 128, 1,
                                              0.1, None)),
