@@ -84,6 +84,20 @@ def test_blocksparse_empty_rows_and_empty_layout():
     ref = oracle.attention_backward(host["q"], host["k"], host["v"], host["do"], True, 0.09, block_mask=bm)
     for a, r in zip((dq, dk, dv), ref):
         assert rel_l2(f64(a), r) <= 1e-2
+    # the dQ kernel that forms the per-row terms gives those rows LSE in base 2 = +inf
+    # and D exactly as the preprocess does, and the same dq, bit for bit
+    ws1 = torch.full((api.workspace_bytes(B, Hq, N),), 0xFF, dtype=torch.uint8, device=dev())
+    ws2 = torch.zeros_like(ws1)
+    dq1, dq2 = torch.empty_like(dq), torch.empty_like(dq)
+    api.backward_steps(g["q"], g["k"], g["v"], o, g["do"], lse, True, 0.09, dq1, dk, dv, ws1,
+                       steps=("pre", "dq"), block_mask=lay.to(dev()))
+    api.backward_steps(g["q"], g["k"], g["v"], o, g["do"], lse, True, 0.09, dq2, dk, dv, ws2,
+                       steps=("pre_dq",), block_mask=lay.to(dev()))
+    torch.cuda.synchronize()
+    rows = B * Hq * N
+    assert torch.equal(ws1[:8 * rows], ws2[:8 * rows])
+    assert np.isposinf(ws2.view(torch.float32)[rows:2 * rows].cpu().numpy().reshape(B, Hq, N)[:, :, :64]).all()
+    assert torch.equal(dq1.view(torch.int16), dq2.view(torch.int16))
     zero = torch.zeros_like(lay)
     o0, l0 = api.forward(g["q"], g["k"], g["v"], False, 0.09, block_mask=zero.to(dev()))
     torch.cuda.synchronize()
