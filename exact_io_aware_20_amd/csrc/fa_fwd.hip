@@ -831,8 +831,9 @@ static hipError_t launch_bf16(const FwdParams& p, hipStream_t stream) {
         // dense d = 128: the non-persistent kernel measured 1.5-2 % faster (its direct
         // fragment addressing and dynamic workgroup dispatch outweigh the fixed cost the
         // persistent form hides at these tile counts)
-        hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, false>), dim3((unsigned)nblk), dim3(FwdCfg<D>::THREADS), 0, stream,
-                           p);
+        if constexpr (D == 128)
+            hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, false>), dim3((unsigned)nblk), dim3(FwdCfg<D>::THREADS), 0,
+                               stream, p);
     } else {
         // sliding window (4 % faster persistent) and d = 64 (2 % faster): one workgroup
         // per compute unit of the device the stream belongs to
@@ -847,7 +848,7 @@ static hipError_t launch_bf16(const FwdParams& p, hipStream_t stream) {
         if (p.window >= 0)
             hipLaunchKernelGGL((fa_fwd_persist_kernel<D, true>), dim3((unsigned)grid), dim3(FwdCfg<D>::THREADS), 0,
                                stream, p);
-        else
+        else if constexpr (D == 64)   // dense d = 128 takes the branch above
             hipLaunchKernelGGL((fa_fwd_persist_kernel<D, false>), dim3((unsigned)grid), dim3(FwdCfg<D>::THREADS), 0,
                                stream, p);
     }
