@@ -395,7 +395,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, uint16_t* smem, co
                     // S one query half at a time: half 0's exponentials run under half 1's
                     // products (the empty asm pins their start inside that region)
                     qk_half_mixed<D, SPARSE ? 2 : 3, 0>(ra, bfr, x[0], 0, [] {});
-                    qk_half_mixed<D, SPARSE ? 2 : 3, 5>(ra, bfr, x[1], 1, [&] {
+                    qk_half_mixed<D, SPARSE ? 2 : 3, 4>(ra, bfr, x[1], 1, [&] {
                         asm volatile("" : "+v"(x[0]));
                         probs(0);
                     });
@@ -414,7 +414,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, uint16_t* smem, co
                 // arithmetic is otherwise free to be placed before it).  Its hand-over is
                 // written after the region: the compiler cannot tell that store from the
                 // region's dO reads apart, and would order every read behind it.
-                acc_half_mixed<D, 5>(ta, bf[0], acc, 0, [&] {                 // dV^T += dO^T P, half 0
+                acc_half_mixed<D, 4>(ta, bf[0], acc, 0, [&] {                 // dV^T += dO^T P, half 0
                     asm volatile("" : "+v"(x[1]));
                     probs(1);
                 });
@@ -450,12 +450,12 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, uint16_t* smem, co
                 // dP = dO V^T one query half at a time, half 0's dS under half 1's products
                 qk_half_mixed<D, SPARSE ? 2 : 3, 0>(ra, bfr, x[0], 0, [] {});
                 __builtin_amdgcn_s_setprio(2);
-                qk_half_mixed<D, SPARSE ? 2 : 3, 5>(ra, bfr, x[1], 1, [&] {
+                qk_half_mixed<D, SPARSE ? 2 : 3, 4>(ra, bfr, x[1], 1, [&] {
                     asm volatile("" : "+v"(x[0]));
                     dsoft(0);
                 });
                 const TrAddr<D> ta(to, lds_addr(st));
-                acc_half_mixed<D, 5>(ta, bf[0], acc, 0, [&] {                 // dK^T += Q^T dS, half 0
+                acc_half_mixed<D, 4>(ta, bf[0], acc, 0, [&] {                 // dK^T += Q^T dS, half 0
                     asm volatile("" : "+v"(x[1]));
                     dsoft(1);
                 });
