@@ -395,7 +395,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, uint16_t* smem, co
                     // S one query half at a time: half 0's exponentials run under half 1's
                     // products (the empty asm pins their start inside that region)
                     qk_half_mixed<D, SPARSE ? 2 : 3, 0>(ra, bfr, x[0], 0, [] {});
-                    qk_half_mixed<D, SPARSE ? 2 : 3, 4>(ra, bfr, x[1], 1, [&] {
+                    qk_half_mixed<D, SPARSE ? 2 : 3, 3>(ra, bfr, x[1], 1, [&] {
                         asm volatile("" : "+v"(x[0]));
                         probs(0);
                     });
@@ -414,7 +414,7 @@ __device__ __forceinline__ void dkdv_tile(const BwdParams& p, uint16_t* smem, co
                 // arithmetic is otherwise free to be placed before it).  Its hand-over is
                 // written after the region: the compiler cannot tell that store from the
                 // region's dO reads apart, and would order every read behind it.
-                acc_half_mixed<D, 4>(ta, bf[0], acc, 0, [&] {                 // dV^T += dO^T P, half 0
+                acc_half_mixed<D, 3>(ta, bf[0], acc, 0, [&] {                 // dV^T += dO^T P, half 0
                     asm volatile("" : "+v"(x[1]));
                     probs(1);
                 });
