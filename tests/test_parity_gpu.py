@@ -485,7 +485,9 @@ def test_preprocess_workspace_contents():
 @pytest.mark.parametrize("shape,causal,mode", [
     ((1, 4, 2, 300, 128), True, "dense"), ((1, 4, 2, 300, 128), False, "dense"),
     ((2, 3, 3, 77, 64), True, "dense"), ((1, 2, 1, 1000, 128), False, "dense"),
-    ((1, 4, 2, 700, 128), True, "window"), ((1, 4, 2, 700, 64), True, "sparse")])
+    ((1, 4, 2, 700, 128), True, "window"), ((1, 4, 2, 700, 64), True, "sparse"),
+    ((1, 6, 2, 333, 64), True, "dense"), ((2, 2, 1, 529, 64), True, "window"),
+    ((1, 4, 4, 640, 128), False, "window"), ((2, 4, 1, 450, 128), False, "sparse")])
 def test_preprocess_dq_equals_preprocess_then_dq(shape, causal, mode):
     # fa_backward_preprocess_dq (the order fa_backward takes) writes the per-row terms of
     # the workspace and dq exactly as fa_backward_preprocess followed by fa_backward_dq do,
